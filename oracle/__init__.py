@@ -1,0 +1,129 @@
+"""Oracle: a plain, slow fp64 CPU implementation of one host-KV attention layer step.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links this
+package; only the tests, the package's smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code with the HIP library.
+
+What it computes (the plain definition; the method reaches the same result, only with a
+different memory layout and transfer schedule — "DirectKV Guide: Zero-Copy KV
+Offloading on GH200 & GB200", FAQ, on the method being lossless):
+
+1. Projections without bias, K = X·Wk and V = X·Wv (and Q = X·Wq, the query the
+   attention uses) — "Paper Notes: DirectKV", section "Fundamental Underlying
+   Technologies / Kernel Fusion (Projection + Attention)", step 1 of the standard path.
+2. The new K/V rows go into the KV cache held in host memory, where they stay and are
+   reused by later steps — same page, section "System Architecture", KV Cache Manager.
+3. Attention softmax(Q·Kᵀ/√d)·V over every cached key a query may see — same page,
+   "Kernel Fusion", step 2 of the standard path.
+
+Where the pages leave a step open, the readings taken are:
+- scale 1/√d (given on "Paper Notes: DirectKV"; the guide's formula drops it);
+- grouped-query attention: query head h reads KV head h // G, G = Hq / Hkv;
+- causal alignment: new token t of sequence b sits at absolute position past_len[b] + t
+  and sees keys 0 .. past_len[b] + t, itself included (a decode step attends to the key
+  it has just appended);
+- no RoPE, no bias, no output projection; W is stored [D, H·d] and applied as X·W;
+  head h occupies columns [h·d, (h+1)·d);
+- rounding happens only where the layer stores: appended cache rows are rounded to the
+  cache dtype (round to nearest, ties to even) and the attention reads the rounded
+  rows; Q and the output are kept in fp64 here.
+
+Arrays: X [B, T, D]; Wq [D, Hq·d]; Wk, Wv [D, Hkv·d]; caches [B, Hkv, cap, d]
+(float32 arrays whose values are exact in the cache dtype, or fp64); past_len int [B].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# significand precision p (hidden bit included), minimum normal exponent, maximum exponent
+_FORMATS = {"f32": (24, -126, 127), "f16": (11, -14, 15), "bf16": (8, -126, 127)}
+
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round fp64 values to the nearest value representable in `dtype`, ties to even
+    (IEEE 754 roundTiesToEven), with gradual underflow and overflow to infinity.
+    Returns fp64 holding the rounded values."""
+    p, emin, emax = _FORMATS[dtype]
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    sel = np.isfinite(x) & (x != 0.0)
+    xs = x[sel]
+    _, e2 = np.frexp(xs)                      # xs = m·2^e2, 1/2 <= |m| < 1
+    lead = np.maximum(e2 - 1, emin)           # exponent of the leading bit; subnormals clamp
+    quantum = np.ldexp(1.0, lead - (p - 1))   # spacing of representable values there
+    r = np.rint(xs / quantum) * quantum       # exact scaling; rint rounds ties to even
+    max_finite = np.ldexp(2.0 - 2.0 ** (1 - p), emax)
+    r = np.where(np.abs(r) > max_finite, np.copysign(np.inf, xs), r)
+    out[sel] = r
+    return out
+
+
+def project(x, w) -> np.ndarray:
+    """X·W in fp64 (library matrix product). x [..., D], w [D, n] -> [..., n]."""
+    return np.matmul(np.asarray(x, dtype=np.float64), np.asarray(w, dtype=np.float64))
+
+
+def append(cache: np.ndarray, rows, past_len, dtype: str) -> None:
+    """Write rows [B, T, H, d] into cache [B, H, cap, d] at token rows
+    [past_len[b], past_len[b] + T), rounded to `dtype`. Nothing else is touched."""
+    rows = np.asarray(rows, dtype=np.float64)
+    B, T, H, d = rows.shape
+    cap = cache.shape[2]
+    assert cache.shape == (B, H, cap, d)
+    for b in range(B):
+        p = int(past_len[b])
+        if p < 0 or p + T > cap:
+            raise ValueError(f"append beyond capacity: past_len={p} T={T} cap={cap}")
+        for g in range(H):
+            cache[b, g, p:p + T, :] = round_to_dtype(rows[b, :, g, :], dtype)
+
+
+def attention(q, kc, vc, past_len, t_index=None, return_lse: bool = False):
+    """Causal grouped-query attention over the cache.
+
+    q [B, n, Hq, d] holds the queries of new tokens t_index[0..n) (default 0..n-1);
+    token t of sequence b sees cache rows 0 .. past_len[b] + t. Returns O [B, n, Hq, d]
+    in fp64 (and log-sum-exp of the scaled scores, [B, n, Hq], if asked)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, n, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    ts = np.arange(n) if t_index is None else np.asarray(t_index, dtype=np.int64)
+    out = np.zeros((B, n, Hq, d), dtype=np.float64)
+    lse = np.zeros((B, n, Hq), dtype=np.float64)
+    if n == 0:
+        return (out, lse) if return_lse else out
+    for b in range(B):
+        L = int(past_len[b])
+        nkeys = L + int(ts.max()) + 1
+        for g in range(Hkv):
+            K = np.asarray(kc[b, g, :nkeys, :], dtype=np.float64)
+            V = np.asarray(vc[b, g, :nkeys, :], dtype=np.float64)
+            for h in range(g * G, (g + 1) * G):
+                for r, t in enumerate(ts):
+                    p = L + int(t)                         # absolute position of the query
+                    s = (K[: p + 1] @ q[b, r, h]) / np.sqrt(d)
+                    m = s.max()
+                    w = np.exp(s - m)
+                    l = w.sum()
+                    out[b, r, h] = (w @ V[: p + 1]) / l
+                    lse[b, r, h] = m + np.log(l)
+    return (out, lse) if return_lse else out
+
+
+def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads: int, dtype: str, t_index=None):
+    """One layer step: project K/V of the T new tokens, append them to the caches
+    (modified in place), then attend for the new tokens t_index (default all).
+    Returns O [B, n, Hq, d] in fp64."""
+    x = np.asarray(x)
+    B, T, D = x.shape
+    Hkv, d = kc.shape[1], kc.shape[3]
+    kn = project(x, wk).reshape(B, T, Hkv, d)
+    vn = project(x, wv).reshape(B, T, Hkv, d)
+    append(kc, kn, past_len, dtype)
+    append(vc, vn, past_len, dtype)
+    ts = np.arange(T) if t_index is None else np.asarray(t_index, dtype=np.int64)
+    q = project(x[:, ts, :], wq).reshape(B, len(ts), n_q_heads, d)
+    return attention(q, kc, vc, past_len, ts)

@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for one host-KV attention layer step.
+
+This module draws random numbers and encodes them in the storage formats the layer uses
+(fp32, IEEE fp16, bfloat16). It holds none of the layer's arithmetic: no projection,
+no append, no softmax. Both the oracle-side tests and the GPU path take their inputs
+from here, and from nowhere else, so that neither side generates data for the other.
+
+Workloads are shaped after the pages' evaluation models: "Paper Notes: DirectKV",
+section "Experiments & Results" (Llama-3.1-8B, 1K-32K contexts), and "DirectKV Guide",
+section "Empirical Benchmarks" (Llama-3-70B at 64K-128K contexts). Values are synthetic:
+X ~ N(0, 1), W ~ N(0, 1/D) (variance 1/D), past K/V ~ N(0, 1), all rounded to the
+layer's dtype. No dataset or trained weight is involved.
+
+Draw order for a named workload (numpy Generator(PCG64(seed))): Wq, Wk, Wv,
+X_prefill, past K, past V (one (b, g) slice at a time), ragged lengths, X_decode[step].
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+def _bf16_round_f32(a: np.ndarray) -> np.ndarray:
+    """Encode float32 values as the nearest bfloat16 (ties to even); returns float32."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def quantize(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Return float32 values exactly representable in `dtype` (input encoding only)."""
+    a = np.asarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return a.copy()
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return _bf16_round_f32(a)
+    raise ValueError(dtype)
+
+
+def to_storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Bit patterns of dtype-exact float32 values: float32 for f32, uint16 otherwise."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return a
+    if dtype == "f16":
+        return a.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        return (a.view(np.uint32) >> 16).astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def from_storage(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Inverse of `to_storage`: decode stored bit patterns to float32 (exact)."""
+    if dtype == "f32":
+        return np.asarray(bits).view(np.float32).astype(np.float32)
+    if dtype == "f16":
+        return np.asarray(bits).view(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+    raise ValueError(dtype)
+
+
+def elem_bytes(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+@dataclasses.dataclass
+class Workload:
+    """Shape of one layer step: B sequences, T new tokens each, past lengths `past`."""
+
+    name: str
+    dtype: str
+    D: int
+    Hq: int
+    Hkv: int
+    d: int
+    B: int
+    T: int
+    past: Optional[List[int]]  # None: ragged, drawn from [past_lo, past_hi]
+    cap: int
+    past_lo: int = 0
+    past_hi: int = 0
+    decode_steps: int = 0
+    seed: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+# The five workloads, in a fixed order; the seed of workload i is 1000 + i.
+# cap = rows per (sequence, kv head) in the host cache, rounded up to a multiple of 64.
+WORKLOADS = [
+    Workload("tiny_f32_prefill128_decode1", "f32", D=256, Hq=4, Hkv=4, d=64,
+             B=1, T=128, past=[0], cap=192, decode_steps=1, seed=1000),
+    Workload("llama8b_decode_b8_L32768_bf16", "bf16", D=4096, Hq=32, Hkv=8, d=128,
+             B=8, T=1, past=[32768] * 8, cap=32832, seed=1001),
+    Workload("llama8b_prefill_T8192_on_L24576_bf16", "bf16", D=4096, Hq=32, Hkv=8, d=128,
+             B=1, T=8192, past=[24576], cap=32768, seed=1002),
+    Workload("long_decode_b4_L96k_128k_f16", "f16", D=4096, Hq=32, Hkv=8, d=128,
+             B=4, T=1, past=None, cap=131136, past_lo=98304, past_hi=131072, seed=1003),
+    Workload("llama70b_prefill_T16384_on_L49152_b2_bf16", "bf16", D=8192, Hq=64, Hkv=8, d=128,
+             B=2, T=16384, past=[49152] * 2, cap=65600, decode_steps=64, seed=1004),
+]
+
+
+def workload(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+class Draw:
+    """Sequential draws for one layer step, in the documented order."""
+
+    def __init__(self, seed: int):
+        self.rng = np.random.Generator(np.random.PCG64(seed))
+
+    def normal(self, shape, std: float, dtype: str) -> np.ndarray:
+        a = self.rng.standard_normal(size=shape, dtype=np.float32)
+        if std != 1.0:
+            a = a * np.float32(std)
+        return quantize(a, dtype)
+
+    def weights(self, D: int, ncols: int, dtype: str) -> np.ndarray:
+        """W ~ N(0, 1/D), stored [D, ncols] and used as X @ W."""
+        return self.normal((D, ncols), D ** -0.5, dtype)
+
+    def lengths(self, B: int, lo: int, hi: int) -> np.ndarray:
+        return self.rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+    def integers(self, shape, lo: int, hi: int) -> np.ndarray:
+        return self.rng.integers(lo, hi, size=shape, endpoint=True).astype(np.float32)
+
+
+def layer_weights(draw: Draw, D: int, Hq: int, Hkv: int, d: int, dtype: str):
+    wq = draw.weights(D, Hq * d, dtype)
+    wk = draw.weights(D, Hkv * d, dtype)
+    wv = draw.weights(D, Hkv * d, dtype)
+    return wq, wk, wv
+
+
+def fill_past(draw: Draw, kc: np.ndarray, vc: np.ndarray, past_len, dtype: str) -> None:
+    """Write N(0, 1) past K (all slices) then past V into rows [0, past_len[b]) of
+    caches shaped [B, Hkv, cap, d]. `kc`/`vc` may be float32 arrays or storage views."""
+    B, Hkv = kc.shape[0], kc.shape[1]
+    d = kc.shape[3]
+    for cache in (kc, vc):
+        for b in range(B):
+            L = int(past_len[b])
+            for g in range(Hkv):
+                vals = draw.normal((L, d), 1.0, dtype)
+                # float32 arrays take the values; uint16 storage views take bit patterns
+                cache[b, g, :L, :] = vals if cache.dtype == np.float32 else to_storage(vals, dtype)
