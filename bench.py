@@ -1,0 +1,264 @@
+"""Benchmark of the host-KV attention layer on one MI355X.
+
+Default workload: a Llama-3-8B-shaped layer decode step in bf16 (D=4096, Hq=32, Hkv=8,
+d=128), batch 8, 32768 past tokens per sequence held in pinned host memory. A step is one
+attn_decode call: q/k/v projection of the new token, append of k/v to the host cache,
+split-KV attention over all 32769 keys, and the combine. Inputs are synthetic (seeded
+N(0,1) activations and past K/V, N(0, 1/D) weights) and resident before timing starts:
+X and W in device memory, the KV cache in pinned host memory, where the method keeps it.
+
+Prints one JSON line. Extra objects: the measured host-link peak (kernel streaming
+read/write of pinned memory), the roofline of the decode kernel, the oracle timed on the
+host cores (cpu_baseline), and a chunked-prefill measurement (8192 new tokens on 24576
+host-resident past tokens) for the prefill half of the metric.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PCIE5_X16_GBPS = 63.0      # published PCIe 5.0 x16 rate per direction (32 GT/s, 128b/130b)
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+PROFILE_NOTE = os.path.join(ROOT, "profiles", "decode_llama8b_b8_L32768_counters.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def tdtype(dt):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+
+
+def to_dev(a, dt):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(tdtype(dt)).cuda()
+
+
+class EventTimer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.s.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e.record()
+        self.e.synchronize()
+        self.ms = self.s.elapsed_time(self.e)
+
+
+def hostlink_peak(dkv, nbytes=1 << 30, reps=5):
+    """Kernel streaming read and write rate of pinned host memory (GB/s)."""
+    import torch
+    cap = nbytes // (128 * 2)
+    buf = dkv.HostKVCache(1, 1, 128, cap, "bf16")
+    ptr = buf.desc.k
+    res = {}
+    for mode in ("read", "write"):
+        dkv.hostlink_stream(ptr, nbytes, mode, 1024)
+        torch.cuda.synchronize()
+        with EventTimer() as t:
+            for _ in range(reps):
+                dkv.hostlink_stream(ptr, nbytes, mode, 1024)
+        res[mode] = nbytes * reps / (t.ms * 1e-3) / 1e9
+    buf.free()
+    return res
+
+
+def setup_decode(dkv, w, seed_off=0):
+    import synth
+    dr = synth.Draw(w.seed + seed_off)
+    wq, wk, wv = synth.layer_weights(dr, w.D, w.Hq, w.Hkv, w.d, w.dtype)
+    past = np.asarray(w.past, dtype=np.int32) if w.past is not None else dr.lengths(w.B, w.past_lo, w.past_hi)
+    x = dr.normal((w.B, 1, w.D), 1.0, w.dtype)
+    cache = dkv.HostKVCache(w.B, w.Hkv, w.d, w.cap, w.dtype)
+    synth.fill_past(dr, cache.k, cache.v, past, w.dtype)
+    return dict(wq=wq, wk=wk, wv=wv, x=x, past=past, cache=cache)
+
+
+def cpu_baseline_decode(w, s, min_seconds=10.0):
+    """The oracle, as it is, on the same decode step, repeated for ~min_seconds."""
+    import oracle
+    import synth
+    import threadpoolctl
+    kc = synth.from_storage(s["cache"].k, w.dtype)
+    vc = synth.from_storage(s["cache"].v, w.dtype)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.layer_step(s["x"], s["wq"], s["wk"], s["wv"], kc, vc, s["past"], w.Hq, w.dtype)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": el / n * 1e6, "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full decode step(s) of the same workload (all {w.B} sequences, "
+                      f"{int(s['past'][0]) + 1} keys each) in fp64 numpy; host has {os.cpu_count()} cpus"}
+
+
+def profile_traffic(kernel_src_hash):
+    """HBM/host bytes per decode launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_NOTE):
+        return None, None
+    vals = {}
+    for line in open(PROFILE_NOTE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha1") != kernel_src_hash:
+        return None, None
+    try:
+        return float(vals["fetch_plus_write_bytes_per_launch"]), float(vals["host_read_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None, None
+
+
+def src_hash(*names):
+    h = hashlib.sha1()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "zero_copy_host_amd", "csrc", n), "rb").read())
+    return h.hexdigest()
+
+
+def bench_prefill(dkv, steps=5, warmup=2):
+    """Chunked prefill of 8192 tokens on 24576 host-resident past tokens (Llama-3-8B layer)."""
+    import torch
+    import synth
+    w = synth.workload("llama8b_prefill_T8192_on_L24576_bf16")
+    dr = synth.Draw(w.seed)
+    wq, wk, wv = synth.layer_weights(dr, w.D, w.Hq, w.Hkv, w.d, w.dtype)
+    past = np.asarray(w.past, dtype=np.int32)
+    x = dr.normal((w.B, w.T, w.D), 1.0, w.dtype)
+    cache = dkv.HostKVCache(w.B, w.Hkv, w.d, w.cap, w.dtype)
+    synth.fill_past(dr, cache.k, cache.v, past, w.dtype)
+    xd, wqd, wkd, wvd = to_dev(x, w.dtype), to_dev(wq.T, w.dtype), to_dev(wk.T, w.dtype), to_dev(wv.T, w.dtype)
+    out = torch.empty((w.B, w.T, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    ws = torch.empty(dkv.workspace_bytes("prefill", cache, w.B, w.T, w.Hq), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        dkv.attn_prefill(cache, xd, wqd, wkd, wvd, past, w.Hq, out, ws)
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for _ in range(steps):
+            dkv.attn_prefill(cache, xd, wqd, wkd, wvd, past, w.Hq, out, ws)
+    ms = t.ms / steps
+    e = 2
+    host_read = 2 * w.Hkv * w.d * e * int(past.sum())
+    host_write = 2 * w.Hkv * w.d * e * w.B * w.T
+    keys = past.astype(np.int64)
+    flops_attn = 4 * w.d * w.Hq * int(np.sum(w.T * keys + w.T * (w.T + 1) // 2))
+    flops_proj = 2 * w.B * w.T * w.D * (w.Hq + 2 * w.Hkv) * w.d
+    cache.free()
+    return {"workload": w.name, "ms_per_step": ms, "tok_per_s": w.B * w.T / (ms * 1e-3),
+            "host_read_GBps_algorithmic": host_read / (ms * 1e-3) / 1e9,
+            "host_write_GBps_algorithmic": host_write / (ms * 1e-3) / 1e9,
+            "tflops": (flops_attn + flops_proj) / (ms * 1e-3) / 1e12, "steps": steps}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_decode_b8_L32768_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="short run for rocprofv3: decode only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer's host-KV path runs on a single MI355X and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    if args.profile:
+        args.no_cpu_baseline = args.no_prefill = True
+
+    import torch
+    import synth
+    import zero_copy_host_amd as dkv
+    torch.cuda.set_device(0)
+    dkv.lib()
+
+    peak = {"read": None, "write": None}
+    if not args.profile:
+        log("measuring host-link peak")
+        peak = hostlink_peak(dkv)
+
+    w = synth.workload(args.workload)
+    assert w.T == 1, "the timed workload is a decode step"
+    log(f"setting up {w.name}")
+    s = setup_decode(dkv, w)
+    xd = to_dev(s["x"], w.dtype)
+    wqd, wkd, wvd = to_dev(s["wq"].T, w.dtype), to_dev(s["wk"].T, w.dtype), to_dev(s["wv"].T, w.dtype)
+    out = torch.empty((w.B, 1, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    ws = torch.empty(dkv.workspace_bytes("decode", s["cache"], w.B, 1, w.Hq), dtype=torch.uint8, device="cuda")
+    past = s["past"]
+
+    def step():
+        # fixed lengths: every step rewrites the same new-token row
+        dkv.attn_decode(s["cache"], xd, wqd, wkd, wvd, past, w.Hq, out, ws)
+
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for _ in range(args.steps):
+            step()
+    ms = t.ms / args.steps
+    torch.cuda.synchronize()
+
+    e = synth.elem_bytes(w.dtype)
+    host_read = 2 * w.Hkv * w.d * e * int(past.sum())            # every past row, K and V, once
+    host_write = 2 * w.Hkv * w.d * e * w.B                       # the new row
+    achieved = host_read / (ms * 1e-3) / 1e9
+    traffic, host_meas = profile_traffic(src_hash("decode.hip"))
+    result = {
+        "metric": "prefill tok/s & decode step us per layer; host-link GB/s vs measured peak",
+        "value": ms * 1e3,
+        "unit": "us per layer decode step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) X and past K/V, N(0,1/D) weights)",
+        "config": {"workload": w.name, "batch": w.B, "past_len": int(past[0]), "new_tokens": 1,
+                   "D": w.D, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "kv_cache": "pinned host memory"},
+        "decode_tok_per_s": w.B / (ms * 1e-3),
+        "roofline": {"bound": "host_link", "kernel": "decode_kernel (+combine) per attn_decode call",
+                     "achieved": achieved, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                     "frac": achieved / PCIE5_X16_GBPS,
+                     "peak_note": "PCIe 5.0 x16 per direction; measured kernel read peak below",
+                     "measured_read_peak": peak["read"],
+                     "frac_of_measured_read_peak": (achieved / peak["read"]) if peak["read"] else None,
+                     "algorithmic_bytes_per_launch": host_read + host_write,
+                     "traffic": traffic, "host_read_bytes_measured": host_meas},
+        "host_link": {"kernel_read_GBps": peak["read"], "kernel_write_GBps": peak["write"]},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline_decode(w, s)
+    s["cache"].free()
+    if not args.no_prefill:
+        log("prefill measurement")
+        result["prefill"] = bench_prefill(dkv)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * directkv.h — C ABI of the host-resident KV-cache attention layer for MI355X (gfx950).
+ *
+ * One transformer layer step: the K/V projection of the new tokens, their append to a
+ * KV cache that lives in pinned host memory, and causal grouped-query attention that
+ * reads that cache in place over the host link (no staging copy in device memory).
+ *
+ * Sources (the pages this library follows):
+ *  [N]  "Paper Notes: DirectKV" — System Architecture (Kernel Generator, Kernel Adaptor,
+ *       Attention Fusion Engine, KV Cache Manager), Key Ideas (1) CPU-memory-aware
+ *       tiling, (2) projection + attention fusion, (3) warp-level pipelining, and
+ *       Fundamental Underlying Technologies / Kernel Fusion (K = X·Wk, V = X·Wv,
+ *       softmax(Q·Kᵀ/√d)·V).
+ *  [G]  "DirectKV Guide: Zero-Copy KV Offloading on GH200 & GB200" — section 1,
+ *       eliminating the GPU staging buffer (host pages mapped into the GPU address space
+ *       and dereferenced by kernels); FAQ (the method is lossless).
+ *
+ * Conventions shared by every call:
+ *  - Element types: dkv_dtype. Activations, weights, cache and output share one dtype.
+ *  - Weights are stored as bias-free linear-layer weights, [out_features, in_features]
+ *    row-major: Wq is [Hq*d, D], Wk and Wv are [Hkv*d, D]; the layer computes X·Wᵀ, so
+ *    head h of Q is columns [h*d, (h+1)*d) of X·Wqᵀ.
+ *  - X is [B, T, D] row-major; the output is [B, T, Hq*d] row-major.
+ *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *  - Causality: new token t of sequence b sits at absolute position past_len[b] + t and
+ *    attends to cache rows 0 .. past_len[b] + t, its own row included.
+ *  - Scores are scaled by 1/sqrt(d); no positional encoding, no bias, no output
+ *    projection.
+ *  - Device pointers (x, w*, out, ws) are caller-owned device memory, 16-byte aligned.
+ *    past_len is a host array of B int32 values, read during the call and never
+ *    written; the caller advances it by T after a successful call.
+ *  - stream: a hipStream_t (0 = the null stream). Calls are asynchronous on it; the
+ *    cache rows a call writes are visible to the host after the stream synchronises.
+ *    Calls touching one cache must be ordered on one stream.
+ *  - Return value: 0 on success, or a negative dkv_status. On error nothing has been
+ *    enqueued, no cache row has been touched, and dkv_last_error() describes why.
+ */
+#ifndef DIRECTKV_H
+#define DIRECTKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DKV_F32 = 0, DKV_F16 = 1, DKV_BF16 = 2 } dkv_dtype;
+
+typedef enum {
+  DKV_OK = 0,
+  DKV_ERR_INVALID_ARG = -1, /* null pointer, size <= 0, misalignment, Hq % Hkv != 0, D unsupported */
+  DKV_ERR_CAPACITY = -2,    /* past_len[b] < 0 or past_len[b] + T > capacity */
+  DKV_ERR_UNSUPPORTED = -3, /* no kernel instance for this dtype / head_dim / group size */
+  DKV_ERR_HOST_ALLOC = -4,  /* pinned host allocation failed */
+  DKV_ERR_HIP = -5,         /* a HIP runtime call failed */
+  DKV_ERR_WORKSPACE = -6    /* ws is null or smaller than attn_workspace_bytes() */
+} dkv_status;
+
+/*
+ * A KV cache in pinned, mapped host memory ([N] System Architecture, KV Cache Manager;
+ * [G] section 1). k and v are host pointers that kernels dereference directly (unified
+ * addressing). Layout of each: [batch][n_kv_heads][capacity][head_dim] row-major, so
+ * the rows of one (sequence, kv head) are contiguous and one token row is
+ * head_dim * element-size bytes. The host may read and write rows between calls.
+ */
+typedef struct dkv_cache {
+  void* k;
+  void* v;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t dtype; /* a dkv_dtype */
+  int32_t reserved;
+} dkv_cache;
+
+/*
+ * Allocate the K and V buffers of a cache with hipHostMalloc (mapped, coherent): pinned
+ * host memory the GPU reads and writes in place. Allocates no device memory. Contents
+ * are undefined; the caller fills past rows through c->k / c->v. Supported head_dim:
+ * 64, 128. capacity must be a positive multiple of 64.
+ * Errors: INVALID_ARG (null out, sizes <= 0, capacity % 64), UNSUPPORTED (head_dim,
+ * dtype), HOST_ALLOC (the allocation failed; *out is zeroed).
+ */
+int kv_alloc_host(dkv_cache* out, int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                  int32_t capacity, int32_t dtype);
+
+/* Free both buffers and zero the descriptor. Idempotent; a zeroed descriptor is OK. */
+int kv_free_host(dkv_cache* c);
+
+/*
+ * Project and append T new tokens per sequence ([N] Kernel Fusion, step 1; KV Cache
+ * Manager): rows [past_len[b], past_len[b] + T) of every kv head g receive
+ * round(X[b]·Wkᵀ) and round(X[b]·Wvᵀ) restricted to columns [g*d, (g+1)*d), rounded to
+ * nearest even in the cache dtype after fp32 accumulation. No other row is written.
+ * x: [batch, T, D]; wk, wv: [Hkv*d, D]. batch must equal c->batch. T = 0 is a no-op.
+ */
+int kv_append(const dkv_cache* c, const void* x, const void* wk, const void* wv,
+              const int32_t* past_len, int32_t batch, int32_t T, int32_t D, void* stream);
+
+/*
+ * Device workspace the attention calls need, in bytes (phase 0 = prefill with T new
+ * tokens, phase 1 = decode with T = 1). It holds the projected queries, this step's new
+ * K/V rows, per-split softmax partials and per-row running softmax state. The caller
+ * allocates it (e.g. as a device tensor) and passes it with its size. Returns 0 for an
+ * invalid argument.
+ */
+size_t attn_workspace_bytes(int32_t phase, const dkv_cache* c, int32_t batch, int32_t T,
+                            int32_t n_q_heads, const int32_t* past_len);
+
+/*
+ * One prefill step of T new tokens per sequence ([N] Attention Fusion Engine, prefill
+ * strategy): Q = X·Wqᵀ into the workspace, the new K/V rows appended to the host cache as
+ * kv_append does, then causal grouped-query attention of the T queries over cache rows
+ * 0 .. past_len[b] + t. Each past host KV row crosses the host link once; the new rows
+ * are written to the host once and are not read back from it. out: [batch, T, Hq*d] in
+ * the cache dtype.
+ */
+int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                 const void* wv, const int32_t* past_len, int32_t batch, int32_t T,
+                 int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/*
+ * One decode step (T = 1) for every sequence ([N] Attention Fusion Engine, decode
+ * strategy): the new token's q, k, v are projected inside the attention kernel, k and v
+ * are stored to host row past_len[b], and the query attends to rows 0 .. past_len[b]
+ * (ragged lengths allowed). Split-KV: each split streams its share of the host rows once
+ * and writes one partial; a combine merges them. out: [batch, 1, Hq*d].
+ */
+int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                const void* wv, const int32_t* past_len, int32_t batch, int32_t D,
+                int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Streaming read (mode 0) or write (mode 1) of `bytes` bytes of pinned host memory at
+ * `host_ptr` by a kernel, the same access path the attention kernels use; measures the
+ * host-link rate the layer is bounded by. bytes must be a multiple of 16 * n_wg;
+ * host_ptr must come from hipHostMalloc. Mode 1 overwrites the buffer.
+ */
+int dkv_hostlink_stream(void* host_ptr, size_t bytes, int32_t mode, int32_t n_wg, void* stream);
+
+/* Thread-local text describing the last non-zero status returned on this thread. */
+const char* dkv_last_error(void);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t dkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIRECTKV_H */

@@ -11,8 +11,9 @@ section "Empirical Benchmarks" (Llama-3-70B at 64K-128K contexts). Values are sy
 X ~ N(0, 1), W ~ N(0, 1/D) (variance 1/D), past K/V ~ N(0, 1), all rounded to the
 layer's dtype. No dataset or trained weight is involved.
 
-Draw order for a named workload (numpy Generator(PCG64(seed))): Wq, Wk, Wv,
-X_prefill, past K, past V (one (b, g) slice at a time), ragged lengths, X_decode[step].
+Draw order for a named workload (numpy Generator(PCG64(seed))): Wq, Wk, Wv, the ragged
+past lengths (if any), X of the first step, past K then past V (one (b, g) slice at a
+time), then X of each later decode step.
 """
 from __future__ import annotations
 
@@ -159,3 +160,35 @@ def fill_past(draw: Draw, kc: np.ndarray, vc: np.ndarray, past_len, dtype: str) 
                 vals = draw.normal((L, d), 1.0, dtype)
                 # float32 arrays take the values; uint16 storage views take bit patterns
                 cache[b, g, :L, :] = vals if cache.dtype == np.float32 else to_storage(vals, dtype)
+
+
+def sparse_sign_weights(draw: Draw, D: int, ncols: int, nnz: int = 8) -> np.ndarray:
+    """Exact-arithmetic weights [D, ncols]: each column has `nnz` entries of +-1 at random
+    rows and zeros elsewhere, so X·W with small-integer X is exact in every dtype."""
+    w = np.zeros((D, ncols), dtype=np.float32)
+    for c in range(ncols):
+        rows = draw.rng.choice(D, size=min(nnz, D), replace=False)
+        w[rows, c] = draw.rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=len(rows))
+    return w
+
+
+def draw_layer(seed: int, B: int, T: int, past, D: int, Hq: int, Hkv: int, d: int, dtype: str,
+               cap: int, exact: bool = False, past_lo: int = 0, past_hi: int = 0):
+    """All inputs of one layer step as float32 arrays exact in `dtype`:
+    wq [D, Hq*d], wk/wv [D, Hkv*d], x [B, T, D], past_len int32 [B], and past caches
+    kp/vp [B, Hkv, cap, d] holding rows [0, past_len[b]) (zeros elsewhere).
+    exact=True draws integer X in [-8, 8] and sparse +-1 weights (exact projections)."""
+    dr = Draw(seed)
+    if exact:
+        wq = sparse_sign_weights(dr, D, Hq * d)
+        wk = sparse_sign_weights(dr, D, Hkv * d)
+        wv = sparse_sign_weights(dr, D, Hkv * d)
+    else:
+        wq, wk, wv = layer_weights(dr, D, Hq, Hkv, d, dtype)
+    past_len = dr.lengths(B, past_lo, past_hi) if past is None else np.asarray(past, dtype=np.int32)
+    x = dr.integers((B, T, D), -8, 8) if exact else dr.normal((B, T, D), 1.0, dtype)
+    kp = np.zeros((B, Hkv, cap, d), dtype=np.float32)
+    vp = np.zeros((B, Hkv, cap, d), dtype=np.float32)
+    fill_past(dr, kp, vp, past_len, dtype)
+    return dict(wq=wq, wk=wk, wv=wv, x=x, past_len=past_len, kp=kp, vp=vp, dtype=dtype,
+                B=B, T=T, D=D, Hq=Hq, Hkv=Hkv, d=d, cap=cap)

@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "directkv.h")
+MAGIC = 0x444B5631   # the mark kv_alloc_host leaves in a descriptor
+
+
+@pytest.fixture(scope="module")
+def dkv():
+    import zero_copy_host_amd as z
+    if not os.path.exists(z.LIB_PATH):
+        from zero_copy_host_amd import build
+        build.build(verbose=False)
+    z.lib()
+    return z
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|int32_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function(dkv):
+    declared = _declared_functions()
+    assert {"kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
+            "attn_decode", "dkv_last_error"} <= set(declared)
+    L = dkv.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(dkv.EXPORTS)
+    assert dkv.version() >= 100
+
+
+def _fake_cache(dkv, B=2, Hkv=2, d=128, cap=128, dtype=2):
+    c = dkv.dkv_cache()
+    c.k, c.v = 0x1000, 0x2000          # never dereferenced: every call below fails validation
+    c.batch, c.n_kv_heads, c.head_dim, c.capacity, c.dtype, c.reserved = B, Hkv, d, cap, dtype, MAGIC
+    return c
+
+
+def _lens(vals):
+    a = np.asarray(vals, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _err(dkv):
+    return dkv.lib().dkv_last_error().decode()
+
+
+def test_alloc_validation(dkv):
+    L, c = dkv.lib(), dkv.dkv_cache()
+    assert L.kv_alloc_host(None, 1, 1, 128, 64, 2) == -1
+    assert L.kv_alloc_host(ctypes.byref(c), 0, 1, 128, 64, 2) == -1
+    assert L.kv_alloc_host(ctypes.byref(c), 1, 1, 128, 100, 2) == -1
+    assert "multiple of 64" in _err(dkv)
+    assert L.kv_alloc_host(ctypes.byref(c), 1, 1, 96, 64, 2) == -3
+    assert L.kv_alloc_host(ctypes.byref(c), 1, 1, 128, 64, 7) == -3
+    assert c.k is None and c.reserved == 0
+    assert L.kv_free_host(ctypes.byref(c)) == 0
+    assert L.kv_free_host(None) == 0
+
+
+def test_call_validation_statuses(dkv):
+    L = dkv.lib()
+    c = _fake_cache(dkv)
+    x = w = out = ws = 0x10000
+    lens, lp = _lens([10, 20])
+    # capacity: 20 + 120 > 128
+    assert L.attn_prefill(ctypes.byref(c), x, w, w, w, lp, 2, 120, 256, 4, out, ws, 1 << 30, None) == -2
+    assert "capacity" in _err(dkv)
+    neg, np_ = _lens([-1, 0])
+    assert L.kv_append(ctypes.byref(c), x, w, w, np_, 2, 1, 256, None) == -2
+    # batch mismatch, bad D, null and misaligned pointers
+    assert L.kv_append(ctypes.byref(c), x, w, w, lp, 3, 1, 256, None) == -1
+    assert L.kv_append(ctypes.byref(c), x, w, w, lp, 2, 1, 100, None) == -1
+    assert L.kv_append(ctypes.byref(c), None, w, w, lp, 2, 1, 256, None) == -1
+    assert L.kv_append(ctypes.byref(c), x + 4, w, w, lp, 2, 1, 256, None) == -1
+    assert L.kv_append(ctypes.byref(c), x, w, w, None, 2, 1, 256, None) == -1
+    # heads: Hq not a multiple of Hkv, unsupported group size
+    assert L.attn_decode(ctypes.byref(c), x, w, w, w, lp, 2, 256, 3, out, ws, 1 << 30, None) == -1
+    assert L.attn_decode(ctypes.byref(c), x, w, w, w, lp, 2, 256, 6, out, ws, 1 << 30, None) == -3
+    # workspace too small
+    assert L.attn_decode(ctypes.byref(c), x, w, w, w, lp, 2, 256, 4, out, ws, 16, None) == -6
+    assert L.attn_prefill(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, 16, None) == -6
+    # descriptor not made by kv_alloc_host
+    bad = _fake_cache(dkv)
+    bad.reserved = 0
+    assert L.attn_decode(ctypes.byref(bad), x, w, w, w, lp, 2, 256, 4, out, ws, 1 << 30, None) == -1
+    assert L.kv_append(None, x, w, w, lp, 2, 1, 256, None) == -1
+    # unsupported head_dim / dtype in a descriptor
+    assert L.kv_append(ctypes.byref(_fake_cache(dkv, d=96)), x, w, w, lp, 2, 1, 256, None) == -3
+    assert L.kv_append(ctypes.byref(_fake_cache(dkv, dtype=5)), x, w, w, lp, 2, 1, 256, None) == -3
+    # hostlink
+    assert L.dkv_hostlink_stream(None, 1024, 0, 4, None) == -1
+    assert L.dkv_hostlink_stream(0x1000, 1000, 0, 4, None) == -1
+    assert L.dkv_hostlink_stream(0x1000, 1024, 2, 4, None) == -1
+
+
+def test_zero_new_tokens_is_a_no_op(dkv):
+    L = dkv.lib()
+    c = _fake_cache(dkv)
+    lens, lp = _lens([10, 20])
+    # T = 0 passes validation and returns before any launch
+    assert L.kv_append(ctypes.byref(c), 0x10000, 0x10000, 0x10000, lp, 2, 0, 256, None) == 0
+    assert L.attn_prefill(ctypes.byref(c), 0x10000, 0x10000, 0x10000, 0x10000, lp, 2, 0, 256, 4,
+                          0x10000, 0x10000, 1 << 30, None) == 0
+
+
+def test_workspace_sizes(dkv):
+    L = dkv.lib()
+    c = _fake_cache(dkv, B=1, Hkv=8, d=128, cap=32768)
+    lens, lp = _lens([24576])
+    ws = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
+    e = 2
+    # queries + new K + new V + fp32 running state (o, m, l) per query row
+    want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 8192 * 32 * 130 * 4
+    assert want <= ws <= want + 4 * 256
+    wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
+    assert 0 < wsd < (1 << 24)
+    assert L.attn_workspace_bytes(2, ctypes.byref(c), 1, 1, 32, lp) == 0
+    assert L.attn_workspace_bytes(1, None, 1, 1, 32, lp) == 0

@@ -1,0 +1,296 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on seeded synthetic inputs.
+
+Small cases span several tiles, several decode splits, several prefill super-chunks and
+ragged tails; exact-arithmetic cases check the append bit for bit; invariants check
+properties the oracle also satisfies (causal perturbation, determinism, phase
+consistency).
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_case import GpuLayer, absdot_rows, compare, compare_rows, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, B, T, past, D, Hq, Hkv, d, dtype, cap=None, exact=False, past_lo=0, past_hi=0):
+    if cap is None:
+        hi = max(past) if past is not None else past_hi
+        cap = ((hi + T + 63) // 64 + 1) * 64
+    return synth.draw_layer(seed, B, T, past, D, Hq, Hkv, d, dtype, cap, exact=exact,
+                            past_lo=past_lo, past_hi=past_hi)
+
+
+def _run_prefill(case, t_index=None, canary=False):
+    g = GpuLayer(case, canary=canary)
+    try:
+        out = g.prefill(case["x"], case["past_len"])
+        kc_g, vc_g = g.cache_k(), g.cache_v()
+    finally:
+        g.free()
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    ref = oracle_step(case, case["x"], case["past_len"], kc, vc, t_index=t_index)
+    if t_index is not None:
+        out = out[:, t_index]
+    return out, ref, kc_g, vc_g, kc, vc
+
+
+# ------------------------------------------------------------------ append
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_append_exact_bitwise_with_canaries(dtype, d):
+    """Exact-arithmetic inputs: appended rows equal the oracle bit for bit; every other
+    row (past rows and NaN canaries) is untouched."""
+    case = _case(11, 3, 37, [5, 0, 130], 256, 4, 2, d, dtype, exact=True)
+    g = GpuLayer(case, canary=True)
+    try:
+        before_k, before_v = g.cache.k.copy(), g.cache.v.copy()
+        g.append(case["x"], case["past_len"])
+        kg, vg = g.cache.k.copy(), g.cache.v.copy()
+    finally:
+        g.free()
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    import oracle
+    B, T = case["B"], case["T"]
+    kn = oracle.project(case["x"], case["wk"]).reshape(B, T, case["Hkv"], d)
+    vn = oracle.project(case["x"], case["wv"]).reshape(B, T, case["Hkv"], d)
+    oracle.append(kc, kn, case["past_len"], dtype)
+    oracle.append(vc, vn, case["past_len"], dtype)
+    for b in range(B):
+        L = int(case["past_len"][b])
+        rows = slice(L, L + T)
+        assert np.array_equal(kg[b, :, rows], synth.to_storage(kc[b, :, rows], dtype))
+        assert np.array_equal(vg[b, :, rows], synth.to_storage(vc[b, :, rows], dtype))
+        for arr_g, arr_b in ((kg, before_k), (vg, before_v)):
+            assert np.array_equal(arr_g[b, :, :L].view(np.uint8), arr_b[b, :, :L].view(np.uint8))
+            assert np.array_equal(arr_g[b, :, L + T:].view(np.uint8), arr_b[b, :, L + T:].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_append_random_values(dtype):
+    case = _case(12, 2, 300, [17, 250], 512, 8, 2, 128, dtype)
+    g = GpuLayer(case)
+    try:
+        g.append(case["x"], case["past_len"])
+        kg, vg = g.cache_k(), g.cache_v()
+    finally:
+        g.free()
+    import oracle
+    B, T, Hkv, d = case["B"], case["T"], case["Hkv"], case["d"]
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    oracle.append(kc, oracle.project(case["x"], case["wk"]).reshape(B, T, Hkv, d), case["past_len"], dtype)
+    oracle.append(vc, oracle.project(case["x"], case["wv"]).reshape(B, T, Hkv, d), case["past_len"], dtype)
+    D = case["D"]
+    ak = absdot_rows(case["x"], case["wk"], Hkv, d)
+    av = absdot_rows(case["x"], case["wv"], Hkv, d)
+    for b in range(B):
+        L = int(case["past_len"][b])
+        compare_rows(kg[b, :, L:L + T], kc[b, :, L:L + T], dtype, ak[b], D, "K rows")
+        compare_rows(vg[b, :, L:L + T], vc[b, :, L:L + T], dtype, av[b], D, "V rows")
+
+
+# ------------------------------------------------------------------ decode
+
+DECODE_CASES = [
+    # B, past, D, Hq, Hkv, d, dtype
+    (1, [0], 256, 4, 4, 64, "f32"),
+    (1, [300], 256, 4, 4, 64, "f32"),
+    (3, [0, 1, 1000], 256, 8, 2, 128, "bf16"),
+    (2, [777, 5000], 512, 16, 2, 64, "f16"),
+    (2, [2000, 3001], 512, 16, 2, 128, "bf16"),   # G = 8
+    (4, [64, 4095, 4096, 12345], 512, 8, 4, 128, "bf16"),
+    (2, [1500, 999], 256, 4, 2, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_CASES, ids=lambda s: f"B{s[0]}-L{max(s[1])}-G{s[3]//s[4]}-d{s[5]}-{s[6]}")
+def test_decode_parity(shape):
+    B, past, D, Hq, Hkv, d, dtype = shape
+    case = _case(13, B, 1, past, D, Hq, Hkv, d, dtype)
+    g = GpuLayer(case, canary=True)
+    try:
+        before = g.cache.k.copy()
+        out = g.decode(case["x"], case["past_len"])
+        kg, vg = g.cache_k(), g.cache_v()
+        after = g.cache.k
+        for b in range(B):
+            L = int(case["past_len"][b])
+            assert np.array_equal(after[b, :, :L].view(np.uint8), before[b, :, :L].view(np.uint8))
+            assert np.array_equal(after[b, :, L + 1:].view(np.uint8), before[b, :, L + 1:].view(np.uint8))
+    finally:
+        g.free()
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    ref = oracle_step(case, case["x"], case["past_len"], kc, vc)
+    compare(out, ref, dtype, f"decode {shape}")
+    ak = absdot_rows(case["x"], case["wk"], Hkv, d)
+    av = absdot_rows(case["x"], case["wv"], Hkv, d)
+    for b in range(B):
+        L = int(case["past_len"][b])
+        compare_rows(kg[b, :, L], kc[b, :, L], dtype, ak[b, :, 0], D, "new K row")
+        compare_rows(vg[b, :, L], vc[b, :, L], dtype, av[b, :, 0], D, "new V row")
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    # B, T, past, D, Hq, Hkv, d, dtype
+    (1, 128, [0], 256, 4, 4, 64, "f32"),             # the tiny fp32 layer
+    (2, 200, [100, 300], 512, 8, 2, 128, "bf16"),
+    (2, 77, [0, 1029], 256, 16, 2, 64, "f16"),       # G = 8, ragged tail
+    (1, 300, [5000], 256, 4, 1, 128, "bf16"),        # two key super-chunks
+    (2, 300, [3000, 4500], 512, 32, 8, 128, "bf16"),  # three super-chunks, 2 pairs per XCD
+    (1, 130, [70], 256, 8, 4, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", PREFILL_CASES, ids=lambda s: f"B{s[0]}-T{s[1]}-L{max(s[2])}-G{s[4]//s[5]}-d{s[6]}-{s[7]}")
+def test_prefill_parity(shape):
+    B, T, past, D, Hq, Hkv, d, dtype = shape
+    case = _case(14, B, T, past, D, Hq, Hkv, d, dtype)
+    out, ref, kg, vg, kc, vc = _run_prefill(case, canary=True)
+    compare(out, ref, dtype, f"prefill {shape}")
+    ak = absdot_rows(case["x"], case["wk"], Hkv, d)
+    av = absdot_rows(case["x"], case["wv"], Hkv, d)
+    for b in range(B):
+        L = int(case["past_len"][b])
+        compare_rows(kg[b, :, L:L + T], kc[b, :, L:L + T], dtype, ak[b], D, "new K rows")
+        compare_rows(vg[b, :, L:L + T], vc[b, :, L:L + T], dtype, av[b], D, "new V rows")
+
+
+def test_tiny_layer_prefill_then_decode():
+    """The tiny fp32 layer: causal prefill of 128 tokens into an empty cache, then one
+    decode step reading the cache the prefill wrote."""
+    w = synth.WORKLOADS[0]
+    case = synth.draw_layer(w.seed, w.B, w.T, w.past, w.D, w.Hq, w.Hkv, w.d, w.dtype, w.cap)
+    xdec = synth.Draw(w.seed + 500).normal((w.B, 1, w.D), 1.0, w.dtype)
+    g = GpuLayer(case)
+    try:
+        out_p = g.prefill(case["x"], case["past_len"])
+        out_d = g.decode(xdec, case["past_len"] + w.T)
+    finally:
+        g.free()
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    ref_p = oracle_step(case, case["x"], case["past_len"], kc, vc)
+    ref_d = oracle_step(case, xdec, case["past_len"] + w.T, kc, vc)
+    compare(out_p, ref_p, "f32", "tiny prefill")
+    compare(out_d, ref_d, "f32", "tiny decode")
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_prefill_causal_perturbation_is_bitwise():
+    case = _case(15, 1, 160, [200], 256, 8, 2, 128, "bf16")
+    g = GpuLayer(case)
+    try:
+        a = g.prefill(case["x"], case["past_len"])
+        x2 = case["x"].copy()
+        x2[:, 100:] = synth.Draw(99).normal(x2[:, 100:].shape, 1.0, "bf16")
+        b = g.prefill(x2, case["past_len"])
+    finally:
+        g.free()
+    assert np.array_equal(a[:, :100], b[:, :100])
+    assert not np.array_equal(a[:, 100:], b[:, 100:])
+
+
+def test_reruns_are_bit_identical():
+    case = _case(16, 2, 1, [3000, 777], 512, 8, 2, 128, "bf16")
+    g = GpuLayer(case)
+    try:
+        d1 = g.decode(case["x"], case["past_len"])
+        d2 = g.decode(case["x"], case["past_len"])
+        casep = _case(17, 1, 200, [1000], 256, 8, 2, 128, "bf16")
+    finally:
+        g.free()
+    assert np.array_equal(d1, d2)
+    gp = GpuLayer(casep)
+    try:
+        p1 = gp.prefill(casep["x"], casep["past_len"])
+        p2 = gp.prefill(casep["x"], casep["past_len"])
+    finally:
+        gp.free()
+    assert np.array_equal(p1, p2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_phase_consistency(dtype):
+    """prefill(T) ~ prefill(T1) + prefill(T - T1) ~ T decode steps (same cache rows)."""
+    T = 40
+    case = _case(18, 2, T, [300, 65], 256, 8, 2, 128, dtype)
+    past = case["past_len"]
+    g1 = GpuLayer(case)
+    try:
+        whole = g1.prefill(case["x"], past)
+    finally:
+        g1.free()
+    g2 = GpuLayer(case)
+    try:
+        a = g2.prefill(case["x"][:, :15], past)
+        b = g2.prefill(case["x"][:, 15:], past + 15)
+    finally:
+        g2.free()
+    g3 = GpuLayer(case)
+    try:
+        steps = [g3.decode(case["x"][:, t:t + 1], past + t) for t in range(T)]
+    finally:
+        g3.free()
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    ref = oracle_step(case, case["x"], past, kc, vc)
+    compare(whole, ref, dtype, "whole")
+    compare(np.concatenate([a, b], axis=1), ref, dtype, "two chunks")
+    compare(np.concatenate(steps, axis=1), ref, dtype, "decode steps")
+
+
+def test_constant_values_give_the_constant():
+    """Wv passes X column 0 (set to 1) scaled by c, past V = c: every output is c."""
+    case = _case(19, 2, 50, [100, 900], 256, 8, 2, 128, "bf16")
+    c = 0.375
+    case["wv"][:] = 0.0
+    case["wv"][0, :] = c
+    case["x"][:, :, 0] = 1.0
+    case["vp"][:] = c
+    g = GpuLayer(case)
+    try:
+        out = g.prefill(case["x"], case["past_len"])
+        outd = g.decode(case["x"][:, :1], case["past_len"] + 50)
+    finally:
+        g.free()
+    assert np.all(np.abs(out - c) <= 2e-3)
+    assert np.all(np.abs(outd - c) <= 2e-3)
+
+
+def test_host_cache_allocates_no_device_memory():
+    import torch
+    import zero_copy_host_amd as dkv
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    free_before, _ = torch.cuda.mem_get_info()
+    cache = dkv.HostKVCache(4, 8, 128, 65536, "bf16")   # 1 GiB of K + V
+    cache.k[0, 0, :4] = 1
+    free_after, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == before
+    assert free_before - free_after < cache.nbytes() // 8
+    cache.free()
+
+
+def test_rejected_calls_enqueue_nothing_and_touch_nothing():
+    import torch
+    import zero_copy_host_amd as dkv
+    case = _case(20, 2, 4, [10, 20], 256, 8, 2, 128, "bf16", cap=64)
+    g = GpuLayer(case, canary=True)
+    try:
+        before = g.cache.k.copy()
+        with pytest.raises(dkv.DirectKVError) as e:
+            g.prefill(np.zeros((2, 60, 256), np.float32), case["past_len"])   # 20 + 60 > 64
+        assert e.value.status == -2
+        ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+        out = torch.empty((2, 1, 8 * 128), dtype=torch.bfloat16, device="cuda")
+        x = torch.zeros((2, 1, 256), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(dkv.DirectKVError) as e:
+            dkv.attn_decode(g.cache, x, g.wq, g.wk, g.wv, case["past_len"], 8, out, ws)
+        assert e.value.status == -6
+        torch.cuda.synchronize()
+        assert np.array_equal(g.cache.k.view(np.uint8), before.view(np.uint8))
+    finally:
+        g.free()

@@ -1,0 +1,177 @@
+"""Python binding of libdirectkv.so: a host-resident KV-cache attention layer for MI355X.
+
+Thin ctypes marshalling over the C ABI declared in include/directkv.h. All of the layer's
+arithmetic runs in the HIP kernels of the library; this module only checks argument
+shapes and passes device pointers, the host cache descriptor and the current HIP stream.
+PyTorch supplies device memory and streams. There is no fallback: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libdirectkv.so")
+
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HOST_ALLOC",
+          -5: "HIP", -6: "WORKSPACE"}
+EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
+           "attn_decode", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+
+
+class DirectKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)} ({status}): {message}")
+        self.status = status
+
+
+class dkv_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m zero_copy_host_amd.build` first")
+        # PyTorch ships its own HIP runtime. Loading torch first makes the library's
+        # libamdhip64.so.7 / libhsa-runtime64.so.1 dependencies bind to those copies, so the
+        # process holds one HIP runtime shared by torch tensors, streams and our kernels.
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+        L.kv_alloc_host.argtypes = [P(dkv_cache), I32, I32, I32, I32, I32]
+        L.kv_free_host.argtypes = [P(dkv_cache)]
+        L.kv_append.argtypes = [P(dkv_cache), VP, VP, VP, P(I32), I32, I32, I32, VP]
+        L.attn_workspace_bytes.argtypes = [I32, P(dkv_cache), I32, I32, I32, P(I32)]
+        L.attn_workspace_bytes.restype = SZ
+        L.attn_prefill.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, I32, VP, VP, SZ, VP]
+        L.attn_decode.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP]
+        L.dkv_hostlink_stream.argtypes = [VP, SZ, I32, I32, VP]
+        L.dkv_last_error.restype = ctypes.c_char_p
+        L.dkv_version.restype = I32
+        for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_decode",
+                     "dkv_hostlink_stream"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DirectKVError(status, lib().dkv_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _lens(past_len, batch: int):
+    a = np.ascontiguousarray(np.asarray(past_len, dtype=np.int32))
+    if a.shape != (batch,):
+        raise ValueError(f"past_len must have shape ({batch},), got {a.shape}")
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class HostKVCache:
+    """K and V buffers [batch, n_kv_heads, capacity, head_dim] in pinned, mapped host memory
+    (hipHostMalloc), read and written in place by the kernels. `k` and `v` are numpy views
+    of the same memory (uint16 bit patterns for f16/bf16, float32 for f32)."""
+
+    def __init__(self, batch: int, n_kv_heads: int, head_dim: int, capacity: int, dtype: str):
+        self.desc = dkv_cache()
+        _check(lib().kv_alloc_host(ctypes.byref(self.desc), batch, n_kv_heads, head_dim, capacity,
+                                   DTYPE_CODES[dtype]))
+        self.dtype = dtype
+        self.shape = (batch, n_kv_heads, capacity, head_dim)
+        ctype = ctypes.c_float if dtype == "f32" else ctypes.c_uint16
+        n = batch * n_kv_heads * capacity * head_dim
+        self.k = np.ctypeslib.as_array(ctypes.cast(self.desc.k, ctypes.POINTER(ctype)), shape=(n,)).reshape(self.shape)
+        self.v = np.ctypeslib.as_array(ctypes.cast(self.desc.v, ctypes.POINTER(ctype)), shape=(n,)).reshape(self.shape)
+
+    @property
+    def batch(self):
+        return self.shape[0]
+
+    @property
+    def n_kv_heads(self):
+        return self.shape[1]
+
+    @property
+    def capacity(self):
+        return self.shape[2]
+
+    @property
+    def head_dim(self):
+        return self.shape[3]
+
+    def nbytes(self) -> int:
+        return 2 * self.k.nbytes
+
+    def free(self) -> None:
+        if self.desc.reserved:
+            self.k = self.v = None
+            lib().kv_free_host(ctypes.byref(self.desc))
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def kv_append(cache: HostKVCache, x, wk, wv, past_len: Sequence[int], stream=None) -> None:
+    """Append round(X·Wkᵀ), round(X·Wvᵀ) at rows [past_len[b], past_len[b]+T). x: [B, T, D]."""
+    B, T, D = x.shape
+    lens, lp = _lens(past_len, B)
+    _check(lib().kv_append(ctypes.byref(cache.desc), _ptr(x), _ptr(wk), _ptr(wv), lp, B, T, D, _stream(stream)))
+
+
+def workspace_bytes(phase: str, cache: HostKVCache, batch: int, T: int, n_q_heads: int) -> int:
+    ph = {"prefill": 0, "decode": 1}[phase]
+    return int(lib().attn_workspace_bytes(ph, ctypes.byref(cache.desc), batch, T, n_q_heads, None))
+
+
+def attn_prefill(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:
+    """One prefill step of T tokens per sequence; out: [B, T, Hq*d] device tensor."""
+    B, T, D = x.shape
+    lens, lp = _lens(past_len, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().attn_prefill(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T, D,
+                              n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:
+    """One decode step; x: [B, 1, D] (or [B, D]); out: [B, 1, Hq*d] device tensor."""
+    B, D = x.shape[0], x.shape[-1]
+    lens, lp = _lens(past_len, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().attn_decode(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
+                             n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def hostlink_stream(host_ptr: int, nbytes: int, mode: str, n_wg: int = 1024, stream=None) -> None:
+    """Kernel streaming read ("read") or write ("write") of pinned host memory."""
+    _check(lib().dkv_hostlink_stream(host_ptr, nbytes, {"read": 0, "write": 1}[mode], n_wg, _stream(stream)))
+
+
+def version() -> int:
+    return int(lib().dkv_version())

@@ -1,0 +1,393 @@
+// C ABI of the host-KV attention layer: argument checks, the kernel adaptor (instance
+// lookup and launch planning), the host cache manager, and dispatch onto a HIP stream.
+//
+// "Paper Notes: DirectKV", System Architecture: the Kernel Generator's pre-built
+// instances over <data type, head dim, tile> are the explicit template instances in the
+// kernel files; the Kernel Adaptor here picks one by dtype, head dim, group size and
+// phase; the KV Cache Manager allocates the pinned host buffers that kernels dereference
+// in place. Every argument is checked before any HIP call, so a rejected call enqueues
+// nothing and leaves the cache untouched.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/directkv.h"
+#include "dkv_internal.h"
+
+using namespace dkv;
+
+namespace {
+
+thread_local std::string g_err;
+constexpr int32_t kMagic = 0x444B5631;  // marks descriptors made by kv_alloc_host
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(int dtype) { return dtype == DKV_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_cache(const dkv_cache* c) {
+  if (!c) return fail(DKV_ERR_INVALID_ARG, "cache descriptor is null");
+  if (c->reserved != kMagic || !c->k || !c->v)
+    return fail(DKV_ERR_INVALID_ARG, "cache descriptor was not made by kv_alloc_host (or was freed)");
+  if (c->dtype < DKV_F32 || c->dtype > DKV_BF16) return fail(DKV_ERR_UNSUPPORTED, "dtype %d", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(DKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", c->head_dim);
+  if (c->batch <= 0 || c->n_kv_heads <= 0 || c->capacity <= 0)
+    return fail(DKV_ERR_INVALID_ARG, "cache sizes must be positive");
+  return DKV_OK;
+}
+
+// common checks of a layer call; T new tokens per sequence
+int check_call(const dkv_cache* c, int32_t batch, int32_t T, int32_t D, const int32_t* past_len,
+               std::initializer_list<const void*> dev_ptrs) {
+  int st = check_cache(c);
+  if (st) return st;
+  if (batch != c->batch) return fail(DKV_ERR_INVALID_ARG, "batch %d != cache batch %d", batch, c->batch);
+  if (batch > kMaxBatch) return fail(DKV_ERR_UNSUPPORTED, "batch %d > %d", batch, kMaxBatch);
+  if (T < 0) return fail(DKV_ERR_INVALID_ARG, "T must be >= 0");
+  if (D <= 0 || D % 64 != 0) return fail(DKV_ERR_INVALID_ARG, "D=%d must be a positive multiple of 64", D);
+  if (!past_len) return fail(DKV_ERR_INVALID_ARG, "past_len is null");
+  for (const void* p : dev_ptrs) {
+    if (!p) return fail(DKV_ERR_INVALID_ARG, "a device pointer is null");
+    if (!aligned16(p)) return fail(DKV_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  for (int b = 0; b < batch; ++b) {
+    if (past_len[b] < 0) return fail(DKV_ERR_CAPACITY, "past_len[%d]=%d < 0", b, past_len[b]);
+    if ((int64_t)past_len[b] + T > c->capacity)
+      return fail(DKV_ERR_CAPACITY, "past_len[%d]=%d + T=%d exceeds capacity %d", b, past_len[b], T, c->capacity);
+  }
+  return DKV_OK;
+}
+
+int check_heads(const dkv_cache* c, int32_t n_q_heads) {
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+    return fail(DKV_ERR_INVALID_ARG, "n_q_heads=%d must be a positive multiple of n_kv_heads=%d", n_q_heads,
+                c->n_kv_heads);
+  const int G = n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(DKV_ERR_UNSUPPORTED, "group size %d (built: 1,2,4,8)", G);
+  return DKV_OK;
+}
+
+// ---- device facts, queried once per process
+int g_cus = 0;
+std::once_flag g_dev_once;
+int cu_count() {
+  std::call_once(g_dev_once, [] {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) g_cus = p.multiProcessorCount;
+    if (g_cus <= 0) g_cus = 256;
+  });
+  return g_cus;
+}
+
+// ---- decode plan: equal key chunks for every workgroup, whatever the lengths
+struct DecodePlan {
+  int chunk;
+  int n_splits;
+  int split_begin[kMaxBatch + 1];
+};
+
+constexpr int kDecodeWgPerCu = 2;
+
+int decode_target_splits(const dkv_cache* c) {
+  // workgroups per kv head so that the whole grid is ~2 per CU
+  return std::max(1, kDecodeWgPerCu * 256 / c->n_kv_heads);
+}
+
+void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, DecodePlan& p) {
+  int64_t keys = 0;
+  for (int b = 0; b < batch; ++b) keys += past_len[b] + 1;
+  const int target = decode_target_splits(c);
+  const int unit = decode_slots(c->dtype, c->head_dim);  // keys one loop iteration consumes
+  int64_t chunk = (keys + target - 1) / target;
+  chunk = std::max<int64_t>(chunk, 2 * unit);
+  chunk = round_up(chunk, unit);
+  p.chunk = (int)chunk;
+  p.n_splits = 0;
+  for (int b = 0; b < batch; ++b) {
+    p.split_begin[b] = p.n_splits;
+    p.n_splits += (int)((past_len[b] + 1 + chunk - 1) / chunk);
+  }
+  p.split_begin[batch] = p.n_splits;
+}
+
+size_t decode_ws_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads) {
+  // sum_b ceil((L_b+1)/chunk) <= keys/chunk + batch <= target + batch
+  const size_t splits = (size_t)decode_target_splits(c) + batch + 1;
+  return round_up(splits * n_q_heads * (c->head_dim + 2) * sizeof(float), 256);
+}
+
+// ---- prefill workspace layout
+struct PrefillWs {
+  size_t q, k_new, v_new, state, total;
+};
+
+PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
+  PrefillWs w;
+  const size_t e = elem_size(c->dtype), d = c->head_dim;
+  w.q = 0;
+  w.k_new = w.q + round_up((size_t)batch * T * n_q_heads * d * e, 256);
+  w.v_new = w.k_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
+  w.state = w.v_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
+  w.total = w.state + round_up((size_t)batch * T * n_q_heads * (d + 2) * sizeof(float), 256);
+  return w;
+}
+
+// keys per super-chunk: the host KV of every (sequence, kv head) pair an XCD serves
+// during one launch must fit about half of that XCD's 4 MB L2
+int superchunk_keys(const dkv_cache* c, int32_t batch) {
+  const int pairs = batch * c->n_kv_heads;
+  const int per_xcd = std::max(1, (pairs + 7) / 8);
+  const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);  // K and V
+  size_t keys = ((size_t)2 << 20) / ((size_t)per_xcd * row_bytes);
+  keys = std::max<size_t>(64, keys / 64 * 64);
+  return (int)std::min<size_t>(keys, 1 << 20);
+}
+
+ProjArgs make_proj(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                   const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
+                   void* q_out, void* k_dev, void* v_dev) {
+  ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.w[0] = wq;
+  a.w[1] = wk;
+  a.w[2] = wv;
+  a.n_seg[0] = wq ? n_q_heads * c->head_dim : 0;
+  a.n_seg[1] = c->n_kv_heads * c->head_dim;
+  a.n_seg[2] = c->n_kv_heads * c->head_dim;
+  for (int s = 0; s < 3; ++s) a.tiles_seg[s] = (a.n_seg[s] + 127) / 128;
+  a.M = batch * T;
+  a.D = D;
+  a.T = T;
+  a.B = batch;
+  a.d = c->head_dim;
+  a.Hkv = c->n_kv_heads;
+  a.cap = c->capacity;
+  a.q_out = q_out;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.k_dev = k_dev;
+  a.v_dev = v_dev;
+  for (int b = 0; b < batch; ++b) a.past_len[b] = past_len[b];
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dkv_version(void) { return 100; }
+
+const char* dkv_last_error(void) { return g_err.c_str(); }
+
+int kv_alloc_host(dkv_cache* out, int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t capacity,
+                  int32_t dtype) {
+  if (!out) return fail(DKV_ERR_INVALID_ARG, "out is null");
+  memset(out, 0, sizeof(*out));
+  if (batch <= 0 || n_kv_heads <= 0 || capacity <= 0)
+    return fail(DKV_ERR_INVALID_ARG, "batch, n_kv_heads and capacity must be positive");
+  if (capacity % 64 != 0) return fail(DKV_ERR_INVALID_ARG, "capacity %d must be a multiple of 64", capacity);
+  if (dtype < DKV_F32 || dtype > DKV_BF16) return fail(DKV_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  const size_t bytes = (size_t)batch * n_kv_heads * capacity * head_dim * elem_size(dtype);
+  if (bytes / elem_size(dtype) / head_dim / capacity != (size_t)batch * n_kv_heads)
+    return fail(DKV_ERR_INVALID_ARG, "cache size overflows");
+  void *k = nullptr, *v = nullptr;
+  const unsigned flags = hipHostMallocMapped | hipHostMallocCoherent;
+  hipError_t e = hipHostMalloc(&k, bytes, flags);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DKV_ERR_HOST_ALLOC, "hipHostMalloc(%zu bytes) for K: %s", bytes, hipGetErrorString(e));
+  }
+  e = hipHostMalloc(&v, bytes, flags);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipHostFree(k);
+    return fail(DKV_ERR_HOST_ALLOC, "hipHostMalloc(%zu bytes) for V: %s", bytes, hipGetErrorString(e));
+  }
+  out->k = k;
+  out->v = v;
+  out->batch = batch;
+  out->n_kv_heads = n_kv_heads;
+  out->head_dim = head_dim;
+  out->capacity = capacity;
+  out->dtype = dtype;
+  out->reserved = kMagic;
+  return DKV_OK;
+}
+
+int kv_free_host(dkv_cache* c) {
+  if (!c) return DKV_OK;
+  if (c->reserved == kMagic) {
+    if (c->k) (void)hipHostFree(c->k);
+    if (c->v) (void)hipHostFree(c->v);
+  }
+  memset(c, 0, sizeof(*c));
+  return DKV_OK;
+}
+
+int kv_append(const dkv_cache* c, const void* x, const void* wk, const void* wv, const int32_t* past_len,
+              int32_t batch, int32_t T, int32_t D, void* stream) {
+  int st = check_call(c, batch, T, D, past_len, {x, wk, wv});
+  if (st) return st;
+  if (T == 0) return DKV_OK;
+  proj_fn f = find_proj(c->dtype, c->head_dim);
+  if (!f) return fail(DKV_ERR_UNSUPPORTED, "no projection instance for dtype %d head_dim %d", c->dtype, c->head_dim);
+  ProjArgs a = make_proj(c, x, nullptr, wk, wv, past_len, batch, T, D, 0, nullptr, nullptr, nullptr);
+  hipError_t e = f(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return DKV_OK;
+}
+
+size_t attn_workspace_bytes(int32_t phase, const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads,
+                            const int32_t* past_len) {
+  (void)past_len;
+  if (check_cache(c) || batch <= 0 || n_q_heads <= 0 || T < 0) return 0;
+  if (phase == 1) return decode_ws_bytes(c, batch, n_q_heads);
+  if (phase == 0) return prefill_layout(c, batch, T, n_q_heads).total;
+  return 0;
+}
+
+int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out, void* ws,
+                size_t ws_bytes, void* stream) {
+  int st = check_call(c, batch, 1, D, past_len, {x, wq, wk, wv, out});
+  if (st) return st;
+  if ((st = check_heads(c, n_q_heads))) return st;
+  if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
+  const size_t need = decode_ws_bytes(c, batch, n_q_heads);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  const int G = n_q_heads / c->n_kv_heads;
+  decode_fn fd = find_decode(c->dtype, c->head_dim, G);
+  combine_fn fc = find_combine(c->dtype, c->head_dim);
+  if (!fd || !fc) return fail(DKV_ERR_UNSUPPORTED, "no decode instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+
+  DecodePlan p;
+  plan_decode(c, past_len, batch, p);
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.wq = wq;
+  a.wk = wk;
+  a.wv = wv;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.part = reinterpret_cast<float*>(ws);
+  a.B = batch;
+  a.D = D;
+  a.Hq = n_q_heads;
+  a.Hkv = c->n_kv_heads;
+  a.cap = c->capacity;
+  a.n_splits = p.n_splits;
+  a.chunk = p.chunk;
+  for (int b = 0; b < batch; ++b) a.past_len[b] = past_len[b];
+  for (int b = 0; b <= batch; ++b) a.split_begin[b] = p.split_begin[b];
+
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.part = a.part;
+  ca.out = out;
+  ca.B = batch;
+  ca.Hq = n_q_heads;
+  ca.n_splits = p.n_splits;
+  for (int b = 0; b <= batch; ++b) ca.split_begin[b] = p.split_begin[b];
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fd(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = fc(ca, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return DKV_OK;
+}
+
+int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                 const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads, void* out,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int st = check_call(c, batch, T, D, past_len, {x, wq, wk, wv, out});
+  if (st) return st;
+  if ((st = check_heads(c, n_q_heads))) return st;
+  if (T == 0) return DKV_OK;
+  const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads);
+  if (!ws || ws_bytes < lay.total || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, lay.total);
+  const int G = n_q_heads / c->n_kv_heads;
+  proj_fn fp = find_proj(c->dtype, c->head_dim);
+  attn_fn fa = find_attn(c->dtype, c->head_dim, G);
+  if (!fp || !fa) return fail(DKV_ERR_UNSUPPORTED, "no prefill instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+
+  char* w = reinterpret_cast<char*>(ws);
+  void* q = w + lay.q;
+  void* kn = w + lay.k_new;
+  void* vn = w + lay.v_new;
+  float* state = reinterpret_cast<float*>(w + lay.state);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, kn, vn);
+  hipError_t e = fp(pa, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+
+  AttnArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.q = q;
+  aa.kc = c->k;
+  aa.vc = c->v;
+  aa.k_new = kn;
+  aa.v_new = vn;
+  aa.state = state;
+  aa.out = out;
+  aa.B = batch;
+  aa.T = T;
+  aa.Hq = n_q_heads;
+  aa.Hkv = c->n_kv_heads;
+  aa.cap = c->capacity;
+  const int rows = attn_rows_per_tile();
+  aa.q_tiles = (T * G + rows - 1) / rows;
+  int max_keys = 0;
+  for (int b = 0; b < batch; ++b) {
+    aa.past_len[b] = past_len[b];
+    max_keys = std::max(max_keys, past_len[b] + T);
+  }
+  const int sk = superchunk_keys(c, batch);
+  const int nsc = (max_keys + sk - 1) / sk;
+  for (int i = 0; i < nsc; ++i) {
+    aa.kc0 = i * sk;
+    aa.kc1 = std::min((i + 1) * sk, max_keys);
+    aa.first = i == 0;
+    aa.last = i == nsc - 1;
+    e = fa(aa, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  return DKV_OK;
+}
+
+int dkv_hostlink_stream(void* host_ptr, size_t bytes, int32_t mode, int32_t n_wg, void* stream) {
+  if (!host_ptr || !aligned16(host_ptr)) return fail(DKV_ERR_INVALID_ARG, "host_ptr null or misaligned");
+  if (mode != 0 && mode != 1) return fail(DKV_ERR_INVALID_ARG, "mode must be 0 (read) or 1 (write)");
+  if (n_wg <= 0 || bytes == 0 || bytes % (16 * (size_t)n_wg) != 0)
+    return fail(DKV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 * n_wg");
+  hipError_t e = launch_hostlink(host_ptr, bytes, mode, n_wg, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hostlink launch");
+  return DKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,346 @@
+// Decode step: one new token per sequence attends to its whole host-resident KV cache.
+//
+// Follows "Paper Notes: DirectKV", System Architecture / Attention Fusion Engine, decode
+// strategy: the single query sweeps every cached (K, V) row, and intermediate output is
+// not re-read from device memory while it does. Each workgroup owns one (sequence b,
+// kv head g, split s): it projects q for the G query heads of the group (and, in the
+// split holding the new position, k and v of the new token, which it stores to the host
+// cache row past_len[b]), then streams its share of host rows exactly once and writes one
+// softmax partial (o, m, l). A small combine kernel merges the partials.
+//
+// On gfx950 the host rows are read by ordinary 16-byte vector loads from pinned mapped
+// memory into registers: this path is a scan of the host link (about G flops per host
+// byte), so latency is hidden by many resident waves with a full iteration of loads in
+// flight each, and no LDS staging is needed for the key/value rows.
+#include "dkv_internal.h"
+
+namespace dkv {
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// dst[r] = scale * sum_k sx[k] * w[(row0 + r) * D + k] for r < nrows (w is [rows, D]).
+// Waves take R rows at a time so that R weight loads per lane are in flight together.
+template <typename T, int R>
+__device__ void project_rows(const float* __restrict__ sx, const T* __restrict__ w, int D,
+                             int row0, int nrows, float* __restrict__ dst, float scale) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int r0 = wave * R; r0 < nrows; r0 += nwaves * R) {
+    float acc[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) acc[i] = 0.f;
+    for (int k = lane * VEC; k < D; k += 64 * VEC) {
+      float xs[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) xs[e] = sx[k + e];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if (r0 + i < nrows) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(w + (size_t)(row0 + r0 + i) * D + k);
+          float f[VEC];
+          Elem<T>::unpack(raw, f);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[i] = fmaf(f[e], xs[e], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) acc[i] = wave_sum(acc[i]);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (r0 + i < nrows) dst[r0 + i] = acc[i] * scale;
+    }
+  }
+}
+
+template <typename T, int DH, int G>
+struct DecodeCfg {
+  static constexpr int VEC = Elem<T>::VEC;
+  static constexpr int LPR = DH / VEC;       // lanes holding one key row
+  static constexpr int RPW = 64 / LPR;       // key rows per wave per step
+  static constexpr int NSLOT = 4 * RPW;      // key rows per workgroup per step
+  static constexpr int U = 4;                // steps per loop iteration (loads in flight)
+  static constexpr int MERGE = NSLOT * G * DH + 2 * NSLOT * G;
+  static constexpr int SMEM = MERGE > kMaxD ? MERGE : kMaxD;
+};
+
+template <typename T, int DH, int G>
+__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+  using C = DecodeCfg<T, DH, G>;
+  constexpr int VEC = C::VEC, LPR = C::LPR, RPW = C::RPW, NSLOT = C::NSLOT, U = C::U;
+  __shared__ float s_buf[C::SMEM];   // activation row, then the per-slot merge area
+  __shared__ float s_q[G * DH];
+  __shared__ float s_kv[2 * DH];     // the new token's k and v (rounded to T)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.y;
+  const int gs = blockIdx.x;
+  int b = 0;
+  while (b + 1 < a.B && a.split_begin[b + 1] <= gs) ++b;
+  const int s = gs - a.split_begin[b];
+  const int L = a.past_len[b];
+  const int k0 = s * a.chunk;
+  const int k1 = min(k0 + a.chunk, L + 1);
+  const bool has_new = (k1 == L + 1);
+  const int kp_end = min(k1, L);            // host rows [k0, kp_end) are read here
+  const size_t bg = (size_t)b * a.Hkv + g;
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.kc) + bg * a.cap * DH;
+  const T* __restrict__ vbase = reinterpret_cast<const T*>(a.vc) + bg * a.cap * DH;
+
+  // ---- projection of this token: q for heads g*G .. g*G+G-1 (and k, v if new)
+  const T* __restrict__ xrow = reinterpret_cast<const T*>(a.x) + (size_t)b * a.D;
+  for (int k = tid; k < a.D; k += blockDim.x) s_buf[k] = Elem<T>::to_float(xrow[k]);
+  __syncthreads();
+  // log2(e)/sqrt(d): scores come out in the base-2 exponent domain
+  const float qscale = 1.4426950408889634f * rsqrtf((float)DH);
+  project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wq), a.D, g * G * DH, G * DH, s_q, qscale);
+  if (has_new) {
+    project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wk), a.D, g * DH, DH, s_kv, 1.f);
+    project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wv), a.D, g * DH, DH, s_kv + DH, 1.f);
+  }
+  __syncthreads();
+  if (has_new) {
+    // storer: round to the cache dtype and write host row L; attention below uses the
+    // rounded values from LDS, never reading the row back over the link
+    T* krow = reinterpret_cast<T*>(a.kc) + (bg * a.cap + L) * DH;
+    T* vrow = reinterpret_cast<T*>(a.vc) + (bg * a.cap + L) * DH;
+    for (int i = tid; i < 2 * DH; i += blockDim.x) {
+      const T r = Elem<T>::from_float(s_kv[i]);
+      if (i < DH) krow[i] = r; else vrow[i - DH] = r;
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * DH; i += blockDim.x) s_kv[i] = Elem<T>::to_float(Elem<T>::from_float(s_kv[i]));
+    __syncthreads();
+  }
+
+  // ---- stream the host rows
+  const int slot = wave * RPW + lane / LPR;
+  const int col = (lane % LPR) * VEC;
+  float q[G][VEC], o[G][VEC], m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) { q[h][e] = s_q[h * DH + col + e]; o[h][e] = 0.f; }
+  }
+
+  auto fetch = [&](int base, uint4 (&kk)[U], uint4 (&vv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * NSLOT + slot;
+      if (key < kp_end) {
+        kk[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * DH + col);
+        vv[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * DH + col);
+      } else {
+        kk[u] = make_uint4(0, 0, 0, 0);
+        vv[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  // one online-softmax update with U key rows per slot; invalid rows carry -inf scores
+  auto consume = [&](int base, const uint4 (&kk)[U], const uint4 (&vv)[U]) {
+    float sc[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VEC];
+      Elem<T>::unpack(kk[u], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc = fmaf(q[h][e], kf[e], acc);
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        sc[u][h] = acc;
+      }
+      const int key = base + u * NSLOT + slot;
+      if (key >= kp_end) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[u][h] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = m[h];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
+      if (mx == -INFINITY) continue;            // nothing valid seen yet
+      const float alpha = exp2f(m[h] - mx);     // exp2(-inf) = 0 on the first update
+      m[h] = mx;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = exp2f(sc[u][h] - mx);
+        l[h] += p;
+        sc[u][h] = p;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[VEC];
+      Elem<T>::unpack(vv[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (m[h] == -INFINITY) continue;
+        const float p = sc[u][h];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+      }
+    }
+  };
+
+  if (k0 < kp_end) {
+    uint4 kc0[U], vc0[U], kc1[U], vc1[U];
+    fetch(k0, kc0, vc0);
+    int base = k0;
+    constexpr int STEP = U * NSLOT;
+    // two register sets: the next iteration's loads are issued before this one computes
+    while (true) {
+      const int nb = base + STEP;
+      if (nb < kp_end) fetch(nb, kc1, vc1);
+      consume(base, kc0, vc0);
+      if (nb >= kp_end) break;
+      base = nb;
+      const int nb2 = base + STEP;
+      if (nb2 < kp_end) fetch(nb2, kc0, vc0);
+      consume(base, kc1, vc1);
+      if (nb2 >= kp_end) break;
+      base = nb2;
+    }
+  }
+
+  // the new token's own key: folded in by slot 0 from LDS
+  if (has_new && slot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc = fmaf(q[h][e], s_kv[col + e], acc);
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      const float mx = fmaxf(m[h], acc);
+      const float alpha = exp2f(m[h] - mx);
+      const float p = exp2f(acc - mx);
+      m[h] = mx;
+      l[h] = l[h] * alpha + p;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(p, s_kv[DH + col + e], o[h][e] * alpha);
+    }
+  }
+
+  // ---- merge the NSLOT slot states of this workgroup and write one partial per head
+  __syncthreads();   // s_buf is reused
+  float* s_o = s_buf;                        // [NSLOT][G][DH]
+  float* s_m = s_buf + NSLOT * G * DH;       // [NSLOT][G]
+  float* s_l = s_m + NSLOT * G;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s_o[(slot * G + h) * DH + col + e] = o[h][e];
+    if (lane % LPR == 0) { s_m[slot * G + h] = m[h]; s_l[slot * G + h] = l[h]; }
+  }
+  __syncthreads();
+  float* part = a.part + ((size_t)gs * a.Hq + (size_t)g * G) * (DH + 2);
+  for (int idx = tid; idx < G * DH; idx += blockDim.x) {
+    const int h = idx / DH, i = idx % DH;
+    float M = -INFINITY;
+    for (int sl = 0; sl < NSLOT; ++sl) M = fmaxf(M, s_m[sl * G + h]);
+    float acc = 0.f, lsum = 0.f;
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      const float ms = s_m[sl * G + h];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      acc = fmaf(s_o[(sl * G + h) * DH + i], w, acc);
+      lsum = fmaf(s_l[sl * G + h], w, lsum);
+    }
+    float* ph = part + (size_t)h * (DH + 2);
+    ph[i] = acc;
+    if (i == 0) { ph[DH] = M; ph[DH + 1] = lsum; }
+  }
+}
+
+// Merge the splits of every (sequence, query head): O = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+template <typename T, int DH>
+__global__ __launch_bounds__(DH) void combine_kernel(const CombineArgs a) {
+  const int b = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+  const int s0 = a.split_begin[b], s1 = a.split_begin[b + 1];
+  float M = -INFINITY;
+  for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part[((size_t)s * a.Hq + h) * (DH + 2) + DH]);
+  float acc = 0.f, lsum = 0.f;
+  for (int s = s0; s < s1; ++s) {
+    const float* p = a.part + ((size_t)s * a.Hq + h) * (DH + 2);
+    const float w = exp2f(p[DH] - M);
+    acc = fmaf(p[i], w, acc);
+    lsum = fmaf(p[DH + 1], w, lsum);
+  }
+  T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.Hq + h) * DH;
+  out[i] = Elem<T>::from_float(acc / lsum);
+}
+
+template <typename T, int DH, int G>
+static hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((decode_kernel<T, DH, G>), dim3(a.n_splits, a.Hkv), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+static hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<T, DH>), dim3(a.B, a.Hq), dim3(DH), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- pre-instantiated kernel table (dtype x head_dim x group size)
+template <typename T, int DH>
+static decode_fn pick_g(int G) {
+  switch (G) {
+    case 1: return launch_decode<T, DH, 1>;
+    case 2: return launch_decode<T, DH, 2>;
+    case 4: return launch_decode<T, DH, 4>;
+    case 8: return launch_decode<T, DH, 8>;
+    default: return nullptr;
+  }
+}
+
+template <typename T>
+static decode_fn pick_d(int d, int G) {
+  if (d == 64) return pick_g<T, 64>(G);
+  if (d == 128) return pick_g<T, 128>(G);
+  return nullptr;
+}
+
+decode_fn find_decode(int dtype, int d, int G) {
+  switch (dtype) {
+    case 0: return pick_d<float>(d, G);
+    case 1: return pick_d<_Float16>(d, G);
+    case 2: return pick_d<__bf16>(d, G);
+    default: return nullptr;
+  }
+}
+
+combine_fn find_combine(int dtype, int d) {
+  if (d != 64 && d != 128) return nullptr;
+  switch (dtype) {
+    case 0: return d == 64 ? launch_combine<float, 64> : launch_combine<float, 128>;
+    case 1: return d == 64 ? launch_combine<_Float16, 64> : launch_combine<_Float16, 128>;
+    case 2: return d == 64 ? launch_combine<__bf16, 64> : launch_combine<__bf16, 128>;
+    default: return nullptr;
+  }
+}
+
+int decode_slots(int dtype, int d) {
+  const int vec = dtype == 0 ? 4 : 8;
+  const int lpr = d / vec;
+  return 4 * (64 / lpr) * 4;  // NSLOT * U: key rows per loop iteration
+}
+
+}  // namespace dkv

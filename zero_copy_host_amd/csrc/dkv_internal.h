@@ -1,0 +1,175 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of the host-KV
+// attention library (gfx950 / CDNA4 only: wave64, 32x32 MFMA, 160 KB LDS per CU).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dkv {
+
+constexpr int kMaxBatch = 256;   // sequences per call (lengths travel in kernel arguments)
+constexpr int kMaxD = 8192;      // model width held in LDS by the decode kernel
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// ------------------------------------------------------------------ element traits
+// Each element type is moved in 16-byte vectors (VEC elements) and computed in fp32.
+template <typename T> struct Elem;
+
+template <> struct Elem<__bf16> {
+  static constexpr int VEC = 8;
+  static constexpr int BYTES = 2;
+  __device__ static inline void unpack(const uint4& r, float (&f)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static inline __bf16 from_float(float f) { return static_cast<__bf16>(f); }
+  __device__ static inline float to_float(__bf16 x) { return static_cast<float>(x); }
+};
+
+template <> struct Elem<_Float16> {
+  static constexpr int VEC = 8;
+  static constexpr int BYTES = 2;
+  __device__ static inline void unpack(const uint4& r, float (&f)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      _Float16 lo, hi;
+      uint16_t l16 = (uint16_t)(w[i] & 0xFFFFu), h16 = (uint16_t)(w[i] >> 16);
+      __builtin_memcpy(&lo, &l16, 2);
+      __builtin_memcpy(&hi, &h16, 2);
+      f[2 * i] = (float)lo;
+      f[2 * i + 1] = (float)hi;
+    }
+  }
+  __device__ static inline _Float16 from_float(float f) { return static_cast<_Float16>(f); }
+  __device__ static inline float to_float(_Float16 x) { return static_cast<float>(x); }
+};
+
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;
+  static constexpr int BYTES = 4;
+  __device__ static inline void unpack(const uint4& r, float (&f)[4]) {
+    f[0] = __uint_as_float(r.x);
+    f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z);
+    f[3] = __uint_as_float(r.w);
+  }
+  __device__ static inline float from_float(float f) { return f; }
+  __device__ static inline float to_float(float x) { return x; }
+};
+
+// ------------------------------------------------------------------ MFMA traits
+// 32x32 output block per wave instruction. Operand slot (lane l, element e) carries
+// row/column l % 32 and reduction index (l / 32) * KPL + e; accumulator register v of
+// lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l % 32 (checked on gfx950).
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  static constexpr int KPL = 8;   // reduction elements per lane per instruction
+  static constexpr int KSTEP = 16;
+  typedef bf16x8 frag;
+  __device__ static inline f32x16 mma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<_Float16> {
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 16;
+  typedef f16x8 frag;
+  __device__ static inline f32x16 mma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 2;
+  typedef float frag;
+  __device__ static inline f32x16 mma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// ------------------------------------------------------------------ launch arguments
+// Y = X·Wᵀ over up to three weight segments (Q, K, V) sharing one activation matrix.
+struct ProjArgs {
+  const void* x;            // [M = B*T, D]
+  const void* w[3];         // segment weights [n_seg, D]; Q, K, V
+  int32_t n_seg[3];         // output features per segment (0 = segment absent)
+  int32_t tiles_seg[3];     // 128-wide column tiles per segment
+  int32_t M, D, T, B, d, Hkv, cap;
+  void* q_out;              // [M, n_seg[0]] device (segment 0)
+  void* kc;                 // host cache K (segment 1), rows [past_len[b] + t]
+  void* vc;                 // host cache V (segment 2)
+  void* k_dev;              // optional device copy of the new K rows [B, Hkv, T, d]
+  void* v_dev;              // optional device copy of the new V rows
+  int32_t past_len[kMaxBatch];
+};
+
+struct DecodeArgs {
+  const void* x;            // [B, D]
+  const void* wq;           // [Hq*d, D]
+  const void* wk;           // [Hkv*d, D]
+  const void* wv;
+  void* kc;                 // host cache
+  void* vc;
+  float* part;              // [n_splits_total][Hq][d + 2]: o (unnormalised), m, l
+  int32_t B, D, Hq, Hkv, cap, n_splits;
+  int32_t past_len[kMaxBatch];
+  int32_t split_begin[kMaxBatch + 1];  // first global split of sequence b
+  int32_t chunk;                       // keys per split
+};
+
+struct CombineArgs {
+  const float* part;
+  void* out;                // [B, Hq*d]
+  int32_t B, Hq, n_splits;
+  int32_t split_begin[kMaxBatch + 1];
+};
+
+// Prefill attention over one super-chunk of keys [kc0, kc1) (absolute positions),
+// updating a per-row running softmax state in device memory.
+struct AttnArgs {
+  const void* q;            // [B, T, Hq, d] device
+  const void* kc;           // host cache (rows < past_len[b] are read from here)
+  const void* vc;
+  const void* k_new;        // [B, Hkv, T, d] device copy of this step's rows
+  const void* v_new;
+  float* state;             // [B, Hkv, T*G rows][d + 2] running o, m, l (log2 domain)
+  void* out;                // [B, T, Hq*d]
+  int32_t B, T, Hq, Hkv, cap;
+  int32_t kc0, kc1;         // super-chunk key range
+  int32_t first, last;      // first super-chunk (no state to read) / last (finalise)
+  int32_t q_tiles;          // row tiles per (b, g)
+  int32_t past_len[kMaxBatch];
+};
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; argument checks happen in the ABI layer.
+typedef hipError_t (*proj_fn)(const ProjArgs&, hipStream_t);
+typedef hipError_t (*decode_fn)(const DecodeArgs&, hipStream_t);
+typedef hipError_t (*combine_fn)(const CombineArgs&, hipStream_t);
+typedef hipError_t (*attn_fn)(const AttnArgs&, hipStream_t);
+
+proj_fn find_proj(int dtype, int d);
+decode_fn find_decode(int dtype, int d, int G);
+combine_fn find_combine(int dtype, int d);
+attn_fn find_attn(int dtype, int d, int G);
+
+int decode_slots(int dtype, int d);  // key rows one decode WG consumes per step
+int attn_rows_per_tile();            // query rows (token x head) per prefill WG
+
+hipError_t launch_hostlink(void* p, size_t bytes, int mode, int n_wg, hipStream_t s);
+
+}  // namespace dkv

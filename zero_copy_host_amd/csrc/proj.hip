@@ -1,0 +1,167 @@
+// Projection GEMM Y = X·Wᵀ for the new tokens of a layer step, over up to three weight
+// segments (Q, K, V) that share the activation matrix X.
+//
+// Follows "Paper Notes: DirectKV", Fundamental Underlying Technologies / Kernel Fusion
+// (K = X·Wk, V = X·Wv) and System Architecture / KV Cache Manager: the K and V rows go
+// straight into the pinned host cache at rows [past_len[b], past_len[b] + T) (the storer
+// role); Q goes to device memory, where the pages keep the queries. Optionally the new
+// K/V rows are also left in device memory, so that attention over them never reads them
+// back across the host link.
+//
+// gfx950 mapping: 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, each
+// wave 2x2 blocks of the 32x32 MFMA; K steps of 32 through a double-buffered LDS tile
+// (X and W both stored k-contiguous, padded by 16 bytes per row against bank conflicts).
+// The epilogue is staged through LDS so every output row leaves as full 16-byte-per-lane
+// contiguous writes (whole host cache lines for K and V).
+#include "dkv_internal.h"
+
+namespace dkv {
+
+template <typename T>
+struct ProjCfg {
+  static constexpr int BM = 128, BN = 128, BK = 32;
+  static constexpr int EB = sizeof(T);
+  static constexpr int VEC = 16 / EB;            // elements per 16-byte chunk
+  static constexpr int LDK = BK + VEC;           // padded row length in LDS (elements)
+  static constexpr int CPR = BK / VEC;           // 16-byte chunks per tile row
+  static constexpr int LOADS = BM * CPR / 256;   // chunks per thread per operand tile
+  static constexpr int LDO = BN + VEC;           // padded output staging row
+  static constexpr int TILE = BM * LDK;          // elements of one operand tile buffer
+  static constexpr int IN_BYTES = 4 * TILE * EB; // X and W, double buffered
+  static constexpr int OUT_BYTES = BM * LDO * EB;
+  static constexpr int SMEM = IN_BYTES > OUT_BYTES ? IN_BYTES : OUT_BYTES;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
+  using C = ProjCfg<T>;
+  using MF = Mfma<T>;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, LDK = C::LDK, CPR = C::CPR;
+  constexpr int LOADS = C::LOADS, KPL = MF::KPL, KSTEP = MF::KSTEP;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+  T* sX = reinterpret_cast<T*>(smem);            // [2][BM][LDK]
+  T* sW = sX + 2 * C::TILE;                      // [2][BN][LDK]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // which segment and column tile this workgroup owns
+  int seg = 0, ty = blockIdx.y;
+  while (seg < 2 && ty >= a.tiles_seg[seg]) { ty -= a.tiles_seg[seg]; ++seg; }
+  const int n0 = ty * BN;
+  const int nseg = a.n_seg[seg];
+  const int m0 = blockIdx.x * BM;
+  const T* __restrict__ X = reinterpret_cast<const T*>(a.x);
+  const T* __restrict__ W = reinterpret_cast<const T*>(a.w[seg]);
+  const int D = a.D;
+
+  uint4 rx[LOADS], rw[LOADS];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int c = tid + j * 256;
+      const int r = c / CPR, kc = (c % CPR) * VEC;
+      const int m = m0 + r, n = n0 + r;
+      rx[j] = (m < a.M) ? *reinterpret_cast<const uint4*>(X + (size_t)m * D + k0 + kc) : make_uint4(0, 0, 0, 0);
+      rw[j] = (n < nseg) ? *reinterpret_cast<const uint4*>(W + (size_t)n * D + k0 + kc) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int c = tid + j * 256;
+      const int r = c / CPR, kc = (c % CPR) * VEC;
+      *reinterpret_cast<uint4*>(sX + buf * C::TILE + r * LDK + kc) = rx[j];
+      *reinterpret_cast<uint4*>(sW + buf * C::TILE + r * LDK + kc) = rw[j];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = D / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const T* tX = sX + buf * C::TILE;
+    const T* tW = sW + buf * C::TILE;
+#pragma unroll
+    for (int ks = 0; ks < BK / KSTEP; ++ks) {
+      typename MF::frag fa[2], fb[2];
+      const int kk = ks * KSTEP + (lane >> 5) * KPL;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const typename MF::frag*>(tX + r * LDK + kk);
+        const int cidx = wn * 64 + i * 32 + (lane & 31);
+        fb[i] = *reinterpret_cast<const typename MF::frag*>(tW + cidx * LDK + kk);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: round to T into an LDS tile, then write whole rows
+  T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + i * 32 + acc_row(v, lane);
+        const int cc = wn * 64 + j * 32 + (lane & 31);
+        sO[r * C::LDO + cc] = Elem<T>::from_float(acc[i][j][v]);
+      }
+  __syncthreads();
+  constexpr int CH = BN / VEC;                   // 16-byte chunks per output row
+  for (int c = tid; c < BM * CH; c += 256) {
+    const int r = c / CH, cc = (c % CH) * VEC;
+    const int m = m0 + r, n = n0 + cc;
+    if (m >= a.M || n >= nseg) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(sO + r * C::LDO + cc);
+    if (seg == 0) {
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.q_out) + (size_t)m * nseg + n) = val;
+    } else {
+      const int b = m / a.T, t = m - b * a.T;
+      const int gg = n / a.d, i = n - gg * a.d;
+      const size_t bgk = (size_t)b * a.Hkv + gg;
+      T* cache = reinterpret_cast<T*>(seg == 1 ? a.kc : a.vc);
+      *reinterpret_cast<uint4*>(cache + (bgk * a.cap + a.past_len[b] + t) * a.d + i) = val;
+      void* dev = seg == 1 ? a.k_dev : a.v_dev;
+      if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
+  const int mt = (a.M + ProjCfg<T>::BM - 1) / ProjCfg<T>::BM;
+  const int nt = a.tiles_seg[0] + a.tiles_seg[1] + a.tiles_seg[2];
+  hipLaunchKernelGGL(proj_kernel<T>, dim3(mt, nt), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+proj_fn find_proj(int dtype, int d) {
+  if (d != 64 && d != 128) return nullptr;
+  switch (dtype) {
+    case 0: return launch_proj<float>;
+    case 1: return launch_proj<_Float16>;
+    case 2: return launch_proj<__bf16>;
+    default: return nullptr;
+  }
+}
+
+}  // namespace dkv
