@@ -160,17 +160,35 @@ def bench_prefill(dkv, steps=5, warmup=2):
         for _ in range(steps):
             dkv.attn_prefill(cache, xd, wqd, wkd, wvd, past, w.Hq, out, ws)
     ms = t.ms / steps
-    e = 2
-    host_read = 2 * w.Hkv * w.d * e * int(past.sum())
-    host_write = 2 * w.Hkv * w.d * e * w.B * w.T
-    keys = past.astype(np.int64)
-    flops_attn = 4 * w.d * w.Hq * int(np.sum(w.T * keys + w.T * (w.T + 1) // 2))
-    flops_proj = 2 * w.B * w.T * w.D * (w.Hq + 2 * w.Hkv) * w.d
+    from zero_copy_host_amd import accounting as acc
+    e = synth.elem_bytes(w.dtype)
+    host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)
+    host_write = acc.host_write_bytes(w.B, w.T, w.Hkv, w.d, e)
+    flops_attn = acc.attention_flops(past, w.T, w.Hq, w.d)
+    flops_proj = acc.projection_flops(w.B, w.T, w.D, w.Hq, w.Hkv, w.d)
     cache.free()
     return {"workload": w.name, "ms_per_step": ms, "tok_per_s": w.B * w.T / (ms * 1e-3),
             "host_read_GBps_algorithmic": host_read / (ms * 1e-3) / 1e9,
             "host_write_GBps_algorithmic": host_write / (ms * 1e-3) / 1e9,
             "tflops": (flops_attn + flops_proj) / (ms * 1e-3) / 1e12, "steps": steps}
+
+
+def calibration_kernels(dkv, nbytes=1 << 30):
+    """Kernels of known traffic for scaling the memory counters: one streaming read and one
+    streaming write of nbytes of pinned host memory, and one device-to-device copy of
+    nbytes (nbytes read + nbytes written in HBM)."""
+    import torch
+    buf = dkv.HostKVCache(1, 1, 128, nbytes // 256, "bf16")
+    dkv.hostlink_stream(buf.desc.k, nbytes, "read", 1024)
+    dkv.hostlink_stream(buf.desc.k, nbytes, "write", 1024)
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    buf.free()
+    print(json.dumps({"calibration_bytes": nbytes}), flush=True)
 
 
 def main():
@@ -181,20 +199,30 @@ def main():
     ap.add_argument("--workload", default="llama8b_decode_b8_L32768_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", action="store_true", help="short run for rocprofv3: decode only")
+    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "calib"],
+                    help="short run for rocprofv3: decode steps only, prefill steps only, or the "
+                         "counter calibration kernels (1 GiB host read, 1 GiB host write, 1 GiB "
+                         "device-to-device copy)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer's host-KV path runs on a single MI355X and this "
               f"build has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
-    if args.profile:
-        args.no_cpu_baseline = args.no_prefill = True
 
     import torch
     import synth
     import zero_copy_host_amd as dkv
     torch.cuda.set_device(0)
     dkv.lib()
+
+    if args.profile == "calib":
+        calibration_kernels(dkv)
+        return
+    if args.profile == "prefill":
+        print(json.dumps({"prefill": bench_prefill(dkv, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.profile:
+        args.no_cpu_baseline = args.no_prefill = True
 
     peak = {"read": None, "write": None}
     if not args.profile:
@@ -225,9 +253,10 @@ def main():
     ms = t.ms / args.steps
     torch.cuda.synchronize()
 
+    from zero_copy_host_amd import accounting as acc
     e = synth.elem_bytes(w.dtype)
-    host_read = 2 * w.Hkv * w.d * e * int(past.sum())            # every past row, K and V, once
-    host_write = 2 * w.Hkv * w.d * e * w.B                       # the new row
+    host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)         # every past row, K and V, once
+    host_write = acc.host_write_bytes(w.B, 1, w.Hkv, w.d, e)     # the new row
     achieved = host_read / (ms * 1e-3) / 1e9
     traffic, host_meas = profile_traffic(src_hash("decode.hip"))
     result = {
