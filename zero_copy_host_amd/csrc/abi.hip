@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -143,17 +144,23 @@ struct PrefillWs {
 PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
   PrefillWs w;
   const size_t e = elem_size(c->dtype), d = c->head_dim;
+  const int G = n_q_heads / std::max(1, c->n_kv_heads);
   w.q = 0;
   w.k_new = w.q + round_up((size_t)batch * T * n_q_heads * d * e, 256);
   w.v_new = w.k_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
   w.state = w.v_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
-  w.total = w.state + round_up((size_t)batch * T * n_q_heads * (d + 2) * sizeof(float), 256);
+  w.total = w.state + round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
   return w;
 }
 
 // keys per super-chunk: the host KV of every (sequence, kv head) pair an XCD serves
 // during one launch must fit about half of that XCD's 4 MB L2
 int superchunk_keys(const dkv_cache* c, int32_t batch) {
+  // tuning override (keys, multiple of 64)
+  if (const char* env = getenv("DIRECTKV_PREFILL_CHUNK")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 64) return (int)(v / 64 * 64);
+  }
   const int pairs = batch * c->n_kv_heads;
   const int per_xcd = std::max(1, (pairs + 7) / 8);
   const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);  // K and V
@@ -362,6 +369,7 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
   aa.cap = c->capacity;
   const int rows = attn_rows_per_tile();
   aa.q_tiles = (T * G + rows - 1) / rows;
+  aa.xcd_group = batch * c->n_kv_heads >= 8;
   int max_keys = 0;
   for (int b = 0; b < batch; ++b) {
     aa.past_len[b] = past_len[b];

@@ -7,18 +7,23 @@
 //
 // gfx950 mapping. The stationary buffer for host KV is an XCD's L2 (4 MB), shared by the
 // 32 CUs of that XCD, rather than one CU's LDS: the host calls this kernel once per key
-// super-chunk [kc0, kc1) sized to fit L2, and workgroup x runs on XCD x % 8 (round-robin
-// dispatch), so all query tiles of one (sequence, kv head) pair sit on one XCD and read the
-// super-chunk from L2 after its first fetch over the link. Each workgroup keeps its query
-// tile in registers, streams the super-chunk through a double-buffered LDS tile, and
-// carries the per-row softmax state (o, m, l) in device memory from one super-chunk launch
-// to the next. Keys below past_len[b] come from the host cache; this step's new keys come
-// from the device copy the projection left, so they never cross the link a second time.
+// super-chunk [kc0, kc1) sized to fit L2, and workgroup i runs on XCD i % 8, so the query
+// tiles of one (sequence, kv head) pair are placed on one XCD and read the super-chunk from
+// L2 after its first fetch over the link. Everything else a workgroup touches (queries,
+// running state, output) is streamed with non-temporal loads and stores so that it does
+// not push the super-chunk out of L2 between rounds of query tiles. Each workgroup keeps
+// 256 query rows in registers (8 waves x 32), sweeps the super-chunk through a
+// double-buffered LDS tile, and carries the per-row softmax state (o, m, l) in device
+// memory from one super-chunk launch to the next. Keys below past_len[b] come from the host
+// cache; this step's new keys come from the device copy the projection left, so they
+// never cross the link a second time.
 //
 // MFMA layout: scores are computed transposed, Sᵀ = K·Qᵀ (32 keys x 32 queries per block),
 // so each lane owns one query column: row max / sum need one cross-half exchange, the
 // accumulators are reused directly as the Pᵀ operand of Oᵀ += Vᵀ·Pᵀ, and Oᵀ rescaling is
-// lane-local. V is transposed once into LDS when a tile is loaded.
+// lane-local. V is transposed once into LDS when a tile is loaded. The softmax reference
+// maximum is raised lazily (only when a score exceeds it by more than 2^8), so the Oᵀ
+// rescale is skipped by whole waves once the maximum has settled.
 #include "dkv_internal.h"
 
 namespace dkv {
@@ -26,36 +31,54 @@ namespace dkv {
 template <typename T, int DH>
 struct AttnCfg {
   static constexpr int KT = 64;                  // keys per LDS tile
-  static constexpr int ROWS = 128;               // query rows per workgroup (4 waves x 32)
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
   static constexpr int EB = sizeof(T);
   static constexpr int VEC = 16 / EB;
   static constexpr int LDK = DH + VEC;           // K tile row (elements), padded
   static constexpr int LDV = KT + 16 / EB;       // Vᵀ tile row (elements), padded
   static constexpr int KTILE = KT * LDK;
   static constexpr int VTILE = DH * LDV;
-  static constexpr int CHUNKS = KT * DH / VEC;   // 16-byte chunks per K (or V) tile
-  static constexpr int LOADS = CHUNKS / 256;     // per thread
+  static constexpr int CPR = DH / VEC;           // 16-byte chunks per key row
+  static constexpr int LOADS = KT * CPR / THREADS;
   static constexpr int DB = DH / 32;             // 32-row blocks of Oᵀ
+  static constexpr int SBLK = (DB * 16 + 2) * 64;  // floats of state per 32 query rows
+  static_assert(LOADS >= 1 && KT * CPR % THREADS == 0, "tile load mapping");
+  static_assert(2 * (KTILE + VTILE) * EB <= 160 * 1024, "LDS budget");
 };
 
+constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max past 2^8
+
 template <typename T, int DH, int G>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
   constexpr int KT = C::KT, VEC = C::VEC, LDK = C::LDK, LDV = C::LDV, LOADS = C::LOADS, DB = C::DB;
-  constexpr int KPL = MF::KPL, KSTEP = MF::KSTEP;
+  constexpr int CPR = C::CPR, KPL = MF::KPL, KSTEP = MF::KSTEP;
   __shared__ __attribute__((aligned(16))) T sK[2][C::KTILE];
   __shared__ __attribute__((aligned(16))) T sV[2][C::VTILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  // workgroup -> (query tile, sequence, kv head); kv head fastest so x % 8 picks the XCD
-  const int g = blockIdx.x % a.Hkv;
-  const int rest = blockIdx.x / a.Hkv;
-  const int b = rest % a.B;
-  const int qt = rest / a.B;
+
+  // workgroup -> (sequence/kv-head pair p, query tile qt). With at least 8 pairs, pair p is
+  // served only by XCD p % 8 (workgroup i runs on XCD i % 8).
+  const int P = a.B * a.Hkv;
+  int p, qt;
+  if (a.xcd_group) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int ppx = (P + 7) >> 3;
+    p = (slot % ppx) * 8 + xcd;
+    qt = slot / ppx;
+    if (p >= P) return;
+  } else {
+    p = blockIdx.x % P;
+    qt = blockIdx.x / P;
+  }
+  const int b = p / a.Hkv, g = p - b * a.Hkv;
   const int L = a.past_len[b];
-  const int nrows = a.T * G;                     // query rows of this (b, g): t*G + hh
+  const int nrows = a.T * G;                     // query rows of this pair: row = t*G + hh
   const int row0 = qt * C::ROWS;
   if (row0 >= nrows) return;
   const int rlast = min(row0 + C::ROWS, nrows) - 1;
@@ -63,45 +86,45 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   const int key_lo = a.kc0;
   const bool work = key_lo < key_hi;
   if (!work && !a.last) return;                  // nothing visible and nothing to finalise
+  const int key_all = L + row0 / G + 1;          // keys below this are visible to every row
 
-  // this lane's query row
-  const int r = row0 + wave * 32 + col;
+  const int r = row0 + wave * 32 + col;          // this lane's query row
   const bool rvalid = r < nrows;
   const int t = rvalid ? r / G : 0;
   const int hh = r - (r / G) * G;
-  const int qpos = L + t;                        // absolute position of the query
-  const size_t bg = (size_t)b * a.Hkv + g;
-  float* st = a.state + (bg * nrows + (rvalid ? r : 0)) * (DH + 2);
+  const int qpos = L + t;
+  const int nblk = (nrows + 31) >> 5;
+  const bool wvalid = (row0 >> 5) + wave < nblk;   // this wave's 32-row block exists
+  float* st = a.state + ((size_t)p * nblk + (wvalid ? (row0 >> 5) + wave : 0)) * C::SBLK;
 
-  // running state: Oᵀ blocks (lane owns its query column), m and l in the log2 domain
   f32x16 o[DB];
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;          // log2 domain, scaled scores
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-  if (!a.first && rvalid) {
+  if (!a.first && wvalid) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] = st[db * 32 + acc_row(v, lane)];
-    m_run = st[DH];
-    l_run = st[DH + 1];
+      for (int v = 0; v < 16; ++v) o[db][v] = __builtin_nontemporal_load(st + (db * 16 + v) * 64 + lane);
+    m_run = __builtin_nontemporal_load(st + DB * 16 * 64 + lane);
+    l_run = __builtin_nontemporal_load(st + (DB * 16 + 1) * 64 + lane);
   }
 
   if (work) {
-    // Qᵀ operand fragments for this lane's query, held for the whole sweep
     typename MF::frag qf[DH / KSTEP];
     {
       const T* qrow = reinterpret_cast<const T*>(a.q) + (((size_t)b * a.T + t) * a.Hq + g * G + hh) * DH;
 #pragma unroll
       for (int ks = 0; ks < DH / KSTEP; ++ks) {
-        if (rvalid) qf[ks] = *reinterpret_cast<const typename MF::frag*>(qrow + ks * KSTEP + half * KPL);
+        if (rvalid) qf[ks] = __builtin_nontemporal_load(reinterpret_cast<const typename MF::frag*>(qrow + ks * KSTEP + half * KPL));
         else qf[ks] = typename MF::frag{};
       }
     }
     const float sl2 = 1.4426950408889634f * rsqrtf((float)DH);   // log2(e)/sqrt(d)
 
+    const size_t bg = (size_t)p;
     const T* __restrict__ kh = reinterpret_cast<const T*>(a.kc) + bg * a.cap * DH;
     const T* __restrict__ vh = reinterpret_cast<const T*>(a.vc) + bg * a.cap * DH;
     const T* __restrict__ kn = reinterpret_cast<const T*>(a.k_new) + bg * a.T * DH;
@@ -111,8 +134,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     auto gload = [&](int j0) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int c = tid + i * 256;
-        const int kr = c / (DH / VEC), kc = (c % (DH / VEC)) * VEC;
+        const int c = tid + i * C::THREADS;
+        const int kr = c / CPR, kc = (c % CPR) * VEC;
         const int j = j0 + kr;
         if (j < key_hi) {
           const T* ks = j < L ? kh + (size_t)j * DH : kn + (size_t)(j - L) * DH;
@@ -128,8 +151,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     auto sstore = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int c = tid + i * 256;
-        const int kr = c / (DH / VEC), kc = (c % (DH / VEC)) * VEC;
+        const int c = tid + i * C::THREADS;
+        const int kr = c / CPR, kc = (c % CPR) * VEC;
         *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = rk[i];
         const T* ve = reinterpret_cast<const T*>(&rv[i]);
 #pragma unroll
@@ -146,58 +169,70 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
       if (more) gload(j0 + KT);
       const T* tK = sK[buf];
       const T* tV = sV[buf];
+      // Sᵀ for the whole tile: KT/32 blocks of 32 keys x 32 queries
+      f32x16 s[KT / 32];
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb) {
-        // Sᵀ block: 32 keys (rows) x 32 queries (columns)
-        f32x16 s;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = 0.f;
+        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < DH / KSTEP; ++ks) {
           const typename MF::frag ka =
               *reinterpret_cast<const typename MF::frag*>(tK + (kb * 32 + col) * LDK + ks * KSTEP + half * KPL);
-          s = MF::mma(ka, qf[ks], s);
+          s[kb] = MF::mma(ka, qf[ks], s[kb]);
         }
-        // scale, causal mask, and the column (query) maximum
-        float mx = -INFINITY;
+      }
+      // mask only where some row of this workgroup cannot see some key of the tile
+      const bool need_mask = (j0 + KT > key_hi) || (j0 + KT > key_all);
+      if (need_mask) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = j0 + kb * 32 + acc_row(v, lane);
-          const bool ok = rvalid && j < key_hi && j <= qpos;
-          s[v] = ok ? s[v] * sl2 : -INFINITY;
-          mx = fmaxf(mx, s[v]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        if (m_new != -INFINITY) {
-          const float alpha = exp2f(m_run - m_new);
-          float ps = 0.f;
+        for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            s[v] = exp2f(s[v] - m_new);
-            ps += s[v];
+            const int j = j0 + kb * 32 + acc_row(v, lane);
+            if (j >= key_hi || j > qpos) s[kb][v] = -INFINITY;
           }
-          ps += __shfl_xor(ps, 32, 64);
-          l_run = l_run * alpha + ps;
-          m_run = m_new;
+      }
+      float mx = -INFINITY;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+      for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-        } else {
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      // lazy reference maximum: raise it only when a score exceeds it by more than 2^8
+      const bool raise = mx > m_run + kLazyRescale;
+      if (__any(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[v] = 0.f;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      }
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s[kb][v] = exp2f(fmaf(s[kb][v], sl2, -mref));
+          ps += s[kb][v];
         }
-        // Oᵀ += Vᵀ · Pᵀ: reduction slot (half, e) of step st is the key held in
-        // accumulator register st*KPL + e of that half
+      l_run += ps + __shfl_xor(ps, 32, 64);
+      // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in
+      // accumulator register stp*KPL + e of that half
+#pragma unroll
+      for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
         for (int stp = 0; stp < 32 / KSTEP; ++stp) {
           typename MF::frag pb;
           if constexpr (KPL == 1) {
-            pb = s[stp];
+            pb = s[kb][stp];
           } else {
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) pb[e] = Elem<T>::from_float(s[stp * KPL + e]);
+            for (int e = 0; e < KPL; ++e) pb[e] = Elem<T>::from_float(s[kb][stp * KPL + e]);
           }
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
@@ -206,9 +241,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
             if constexpr (KPL == 1) {
               va = vrow[acc_row(stp, lane)];
             } else {
-              // keys acc_row(stp*8 + e): two runs of four consecutive keys
-#pragma unroll
-              for (int e = 0; e < KPL; ++e) va[e] = vrow[acc_row(stp * KPL + e, lane)];
+              // keys 16*stp + 4*half + {0..3} and 16*stp + 8 + 4*half + {0..3}
+              const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * stp + 4 * half);
+              const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * stp + 8 + 4 * half);
+              const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+              __builtin_memcpy(&va, &w, 16);
             }
             o[db] = MF::mma(va, pb, o[db]);
           }
@@ -220,28 +257,30 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     }
   }
 
-  if (!rvalid) return;
   if (a.last) {
+    if (!rvalid) return;
     const float inv = 1.f / l_run;
     T* orow = reinterpret_cast<T*>(a.out) + (((size_t)b * a.T + t) * a.Hq + g * G + hh) * DH;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) orow[db * 32 + acc_row(v, lane)] = Elem<T>::from_float(o[db][v] * inv);
-  } else {
+      for (int v = 0; v < 16; ++v)
+        __builtin_nontemporal_store(Elem<T>::from_float(o[db][v] * inv), orow + db * 32 + acc_row(v, lane));
+  } else if (wvalid) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) st[db * 32 + acc_row(v, lane)] = o[db][v];
-    st[DH] = m_run;
-    st[DH + 1] = l_run;
+      for (int v = 0; v < 16; ++v) __builtin_nontemporal_store(o[db][v], st + (db * 16 + v) * 64 + lane);
+    __builtin_nontemporal_store(m_run, st + DB * 16 * 64 + lane);
+    __builtin_nontemporal_store(l_run, st + (DB * 16 + 1) * 64 + lane);
   }
 }
 
 template <typename T, int DH, int G>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-  const int grid = a.q_tiles * a.B * a.Hkv;
-  hipLaunchKernelGGL((attn_kernel<T, DH, G>), dim3(grid), dim3(256), 0, s, a);
+  const int P = a.B * a.Hkv;
+  const int grid = a.xcd_group ? 8 * ((P + 7) / 8) * a.q_tiles : P * a.q_tiles;
+  hipLaunchKernelGGL((attn_kernel<T, DH, G>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -272,6 +311,11 @@ attn_fn find_attn(int dtype, int d, int G) {
   }
 }
 
-int attn_rows_per_tile() { return 128; }
+int attn_rows_per_tile() { return 256; }
+
+size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G) {
+  const size_t nblk = ((size_t)T * G + 31) / 32;
+  return (size_t)batch * n_kv_heads * nblk * (size_t)((d / 32) * 16 + 2) * 64 * sizeof(float);
+}
 
 }  // namespace dkv

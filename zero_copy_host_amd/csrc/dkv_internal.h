@@ -146,12 +146,13 @@ struct AttnArgs {
   const void* vc;
   const void* k_new;        // [B, Hkv, T, d] device copy of this step's rows
   const void* v_new;
-  float* state;             // [B, Hkv, T*G rows][d + 2] running o, m, l (log2 domain)
+  float* state;             // running o, m, l (log2 domain) per 32 query rows: see attn_state_bytes
   void* out;                // [B, T, Hq*d]
   int32_t B, T, Hq, Hkv, cap;
   int32_t kc0, kc1;         // super-chunk key range
   int32_t first, last;      // first super-chunk (no state to read) / last (finalise)
   int32_t q_tiles;          // row tiles per (b, g)
+  int32_t xcd_group;        // 1: pair p is served only by XCD p % 8 (needs B*Hkv >= 8)
   int32_t past_len[kMaxBatch];
 };
 
@@ -169,6 +170,7 @@ attn_fn find_attn(int dtype, int d, int G);
 
 int decode_slots(int dtype, int d);  // key rows one decode WG consumes per step
 int attn_rows_per_tile();            // query rows (token x head) per prefill WG
+size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G);
 
 hipError_t launch_hostlink(void* p, size_t bytes, int mode, int n_wg, hipStream_t s);
 
