@@ -37,9 +37,12 @@ struct AttnCfg {
   static constexpr int EB = sizeof(T);
   static constexpr int VEC = 16 / EB;
   static constexpr int LDK = DH + VEC;           // K tile row (elements), padded
-  static constexpr int LDV = KT + 16 / EB;       // Vᵀ tile row (elements), padded
+  // 16-bit types keep V row-major ([key][d]) and read Vᵀ fragments with the gfx950 LDS
+  // transpose read; fp32 stores Vᵀ ([d][key]) at load time instead.
+  static constexpr bool VROW = EB == 2;
+  static constexpr int LDV = VROW ? DH + 16 : KT + 16 / EB;
   static constexpr int KTILE = KT * LDK;
-  static constexpr int VTILE = DH * LDV;
+  static constexpr int VTILE = VROW ? KT * LDV : DH * LDV;
   static constexpr int CPR = DH / VEC;           // 16-byte chunks per key row
   static constexpr int LOADS = KT * CPR / THREADS;
   static constexpr int DB = DH / 32;             // 32-row blocks of Oᵀ
@@ -154,9 +157,13 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
         const int c = tid + i * C::THREADS;
         const int kr = c / CPR, kc = (c % CPR) * VEC;
         *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = rk[i];
-        const T* ve = reinterpret_cast<const T*>(&rv[i]);
+        if constexpr (C::VROW) {
+          *reinterpret_cast<uint4*>(&sV[buf][kr * LDV + kc]) = rv[i];
+        } else {
+          const T* ve = reinterpret_cast<const T*>(&rv[i]);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sV[buf][(kc + e) * LDV + kr] = ve[e];
+          for (int e = 0; e < VEC; ++e) sV[buf][(kc + e) * LDV + kr] = ve[e];
+        }
       }
     };
 
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       const bool raise = mx > m_run + kLazyRescale;
       if (__any(raise)) {
         const float m_new = raise ? mx : m_run;
-        const float alpha = raise ? exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          s[kb][v] = exp2f(fmaf(s[kb][v], sl2, -mref));
+          s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mref));
           ps += s[kb][v];
         }
       l_run += ps + __shfl_xor(ps, 32, 64);
@@ -237,15 +244,26 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             typename MF::frag va;
-            const T* vrow = tV + (db * 32 + col) * LDV + kb * 32;
-            if constexpr (KPL == 1) {
-              va = vrow[acc_row(stp, lane)];
+            if constexpr (C::VROW) {
+              // lane needs V[keys 16*stp + 4*half + {0..3}, +8 + ...][d = db*32 + col]. The
+              // transpose read gives result lane i (of 16) value k from source lane 4k + i/4,
+              // element i % 4; so source lane 4k + q of each 16-lane group points at
+              // V[kbase + k][d0 + 4q], with d0 the group's first column.
+              const int li = lane & 15, kk = li >> 2, qq = li & 3;
+              const int d0 = db * 32 + (lane & 16);
+              const int kbase = kb * 32 + 16 * stp + 4 * half;
+              const T* src0 = tV + (kbase + kk) * LDV + d0 + 4 * qq;
+              const T* src1 = src0 + 8 * LDV;
+              typedef short v4s __attribute__((ext_vector_type(4)));
+              const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4s*)(src0));
+              const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4s*)(src1));
+              __builtin_memcpy(&va, &lo, 8);
+              __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
             } else {
-              // keys 16*stp + 4*half + {0..3} and 16*stp + 8 + 4*half + {0..3}
-              const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * stp + 4 * half);
-              const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * stp + 8 + 4 * half);
-              const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-              __builtin_memcpy(&va, &w, 16);
+              const T* vrow = tV + (db * 32 + col) * LDV + kb * 32;
+              va = vrow[acc_row(stp, lane)];
             }
             o[db] = MF::mma(va, pb, o[db]);
           }
