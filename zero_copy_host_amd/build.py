@@ -26,7 +26,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-result",
-]
+] + os.environ.get("DKV_EXTRA_FLAGS", "").split()
 
 
 def _sources():

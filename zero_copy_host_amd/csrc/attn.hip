@@ -28,9 +28,17 @@
 
 namespace dkv {
 
+// Build-time tunables (defaults are the tuned values).
+#ifndef DKV_ATTN_KT
+#define DKV_ATTN_KT 64
+#endif
+#ifndef DKV_ATTN_SETPRIO
+#define DKV_ATTN_SETPRIO 0
+#endif
+
 template <typename T, int DH>
 struct AttnCfg {
-  static constexpr int KT = 64;                  // keys per LDS tile
+  static constexpr int KT = sizeof(T) == 2 ? DKV_ATTN_KT : 64;   // keys per LDS tile
   static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
@@ -178,6 +186,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       const T* tV = sV[buf];
       // Sᵀ for the whole tile: KT/32 blocks of 32 keys x 32 queries
       f32x16 s[KT / 32];
+      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
@@ -189,6 +198,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
           s[kb] = MF::mma(ka, qf[ks], s[kb]);
         }
       }
+      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       // mask only where some row of this workgroup cannot see some key of the tile
       const bool need_mask = (j0 + KT > key_hi) || (j0 + KT > key_all);
       if (need_mask) {
@@ -230,6 +240,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       l_run += ps + __shfl_xor(ps, 32, 64);
       // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in
       // accumulator register stp*KPL + e of that half
+      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
@@ -269,6 +280,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
           }
         }
       }
+      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       if (more) sstore(buf ^ 1);
       __syncthreads();
       buf ^= 1;
