@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PCIE5_X16_GBPS = 63.0      # published PCIe 5.0 x16 rate per direction (32 GT/s, 128b/130b)
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense
 PROFILE_NOTE = os.path.join(ROOT, "profiles", "decode_llama8b_b8_L32768_counters.txt")
 
 
@@ -139,38 +140,100 @@ def src_hash(*names):
     return h.hexdigest()
 
 
-def bench_prefill(dkv, steps=5, warmup=2):
-    """Chunked prefill of 8192 tokens on 24576 host-resident past tokens (Llama-3-8B layer)."""
-    import torch
+def _layer_setup(dkv, w, seed_extra=0):
+    """Weights, lengths, X of the first step and the filled host cache for workload w."""
     import synth
-    w = synth.workload("llama8b_prefill_T8192_on_L24576_bf16")
-    dr = synth.Draw(w.seed)
+    dr = synth.Draw(w.seed + seed_extra)
     wq, wk, wv = synth.layer_weights(dr, w.D, w.Hq, w.Hkv, w.d, w.dtype)
-    past = np.asarray(w.past, dtype=np.int32)
+    past = np.asarray(w.past, dtype=np.int32) if w.past is not None else dr.lengths(w.B, w.past_lo, w.past_hi)
     x = dr.normal((w.B, w.T, w.D), 1.0, w.dtype)
     cache = dkv.HostKVCache(w.B, w.Hkv, w.d, w.cap, w.dtype)
     synth.fill_past(dr, cache.k, cache.v, past, w.dtype)
-    xd, wqd, wkd, wvd = to_dev(x, w.dtype), to_dev(wq.T, w.dtype), to_dev(wk.T, w.dtype), to_dev(wv.T, w.dtype)
-    out = torch.empty((w.B, w.T, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
-    ws = torch.empty(dkv.workspace_bytes("prefill", cache, w.B, w.T, w.Hq), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        dkv.attn_prefill(cache, xd, wqd, wkd, wvd, past, w.Hq, out, ws)
-    torch.cuda.synchronize()
-    with EventTimer() as t:
-        for _ in range(steps):
-            dkv.attn_prefill(cache, xd, wqd, wkd, wvd, past, w.Hq, out, ws)
-    ms = t.ms / steps
+    dev = dict(x=to_dev(x, w.dtype), wq=to_dev(wq.T, w.dtype), wk=to_dev(wk.T, w.dtype), wv=to_dev(wv.T, w.dtype))
+    return past, cache, dev, dr
+
+
+def _prefill_stats(w, past, ms, peak_read):
+    import synth
     from zero_copy_host_amd import accounting as acc
     e = synth.elem_bytes(w.dtype)
     host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)
     host_write = acc.host_write_bytes(w.B, w.T, w.Hkv, w.d, e)
-    flops_attn = acc.attention_flops(past, w.T, w.Hq, w.d)
-    flops_proj = acc.projection_flops(w.B, w.T, w.D, w.Hq, w.Hkv, w.d)
+    flops = acc.attention_flops(past, w.T, w.Hq, w.d) + acc.projection_flops(w.B, w.T, w.D, w.Hq, w.Hkv, w.d)
+    mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_step": ms, "tok_per_s": w.B * w.T / (ms * 1e-3),
+            "tflops": tflops, "mfma_peak_tflops": mfma_peak, "mfma_frac": tflops / mfma_peak,
+            "host_read_bytes": host_read, "host_write_bytes": host_write,
+            "host_read_floor_ms": host_read / (peak_read * 1e9) * 1e3 if peak_read else None,
+            "mfma_floor_ms": flops / (mfma_peak * 1e12) * 1e3}
+
+
+def _decode_stats(w, past, ms, peak_read):
+    import synth
+    from zero_copy_host_amd import accounting as acc
+    e = synth.elem_bytes(w.dtype)
+    host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)
+    gbps = host_read / (ms * 1e-3) / 1e9
+    return {"us_per_step": ms * 1e3, "tok_per_s": w.B / (ms * 1e-3), "host_read_bytes": host_read,
+            "host_read_GBps": gbps, "frac_of_measured_read_peak": gbps / peak_read if peak_read else None,
+            "frac_of_pcie5_x16": gbps / PCIE5_X16_GBPS}
+
+
+def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0):
+    """Time the prefill step of workload `name` (fixed past lengths, so every step rewrites the
+    same rows); optionally follow it with real decode steps at advancing lengths."""
+    import torch
+    import synth
+    w = synth.workload(name)
+    past, cache, dev, dr = _layer_setup(dkv, w)
+    out = torch.empty((w.B, w.T, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    ws = torch.empty(dkv.workspace_bytes("prefill", cache, w.B, w.T, w.Hq), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        dkv.attn_prefill(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for _ in range(steps):
+            dkv.attn_prefill(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    res = {"workload": name, "steps": steps, **_prefill_stats(w, past, t.ms / steps, peak_read)}
+    if decode_steps:
+        del out, ws
+        xs = [to_dev(dr.normal((w.B, 1, w.D), 1.0, w.dtype), w.dtype) for _ in range(decode_steps)]
+        outd = torch.empty((w.B, 1, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+        wsd = torch.empty(dkv.workspace_bytes("decode", cache, w.B, 1, w.Hq), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        with EventTimer() as t:
+            for s_ in range(decode_steps):
+                dkv.attn_decode(cache, xs[s_], dev["wq"], dev["wk"], dev["wv"], past + w.T + s_, w.Hq, outd, wsd)
+        ms = t.ms / decode_steps
+        mid = past + w.T + decode_steps // 2
+        res["decode"] = {"steps": decode_steps, "past_len_first": int(past[0] + w.T),
+                         **_decode_stats(w, mid, ms, peak_read)}
     cache.free()
-    return {"workload": w.name, "ms_per_step": ms, "tok_per_s": w.B * w.T / (ms * 1e-3),
-            "host_read_GBps_algorithmic": host_read / (ms * 1e-3) / 1e9,
-            "host_write_GBps_algorithmic": host_write / (ms * 1e-3) / 1e9,
-            "tflops": (flops_attn + flops_proj) / (ms * 1e-3) / 1e12, "steps": steps}
+    return res
+
+
+def run_decode(dkv, name, steps=10, warmup=2, peak_read=None):
+    """Time a decode step of workload `name` at fixed past lengths."""
+    import torch
+    import synth
+    w = synth.workload(name)
+    past, cache, dev, _ = _layer_setup(dkv, w)
+    out = torch.empty((w.B, 1, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    ws = torch.empty(dkv.workspace_bytes("decode", cache, w.B, 1, w.Hq), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for _ in range(steps):
+            dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    cache.free()
+    return {"workload": name, "steps": steps, "past_len": [int(x) for x in past],
+            **_decode_stats(w, past, t.ms / steps, peak_read)}
+
+
+def bench_prefill(dkv, steps=5, warmup=2):
+    return run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps, warmup)
 
 
 def calibration_kernels(dkv, nbytes=1 << 30):
@@ -284,8 +347,20 @@ def main():
         result["cpu_baseline"] = cpu_baseline_decode(w, s)
     s["cache"].free()
     if not args.no_prefill:
-        log("prefill measurement")
-        result["prefill"] = bench_prefill(dkv)
+        pr = peak["read"]
+        log("other workloads: tiny fp32 layer")
+        tiny = run_prefill(dkv, "tiny_f32_prefill128_decode1", steps=20, warmup=3, peak_read=pr, decode_steps=1)
+        log("8B chunked prefill")
+        result["prefill"] = run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=5, warmup=2, peak_read=pr)
+        log("long-context fp16 decode")
+        longd = run_decode(dkv, "long_decode_b4_L96k_128k_f16", steps=6, warmup=1, peak_read=pr)
+        log("70B prefill + 64 decode steps")
+        big = run_prefill(dkv, "llama70b_prefill_T16384_on_L49152_b2_bf16", steps=2, warmup=1, peak_read=pr,
+                          decode_steps=64)
+        result["workloads"] = {"tiny_f32_prefill128_decode1": tiny,
+                               "llama8b_prefill_T8192_on_L24576_bf16": result["prefill"],
+                               "long_decode_b4_L96k_128k_f16": longd,
+                               "llama70b_prefill_T16384_on_L49152_b2_bf16": big}
     print(json.dumps(result), flush=True)
 
 
