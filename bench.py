@@ -180,7 +180,8 @@ def _decode_stats(w, past, ms, peak_read):
             "frac_of_pcie5_x16": gbps / PCIE5_X16_GBPS}
 
 
-def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0):
+def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, variant="fused",
+                ablations=()):
     """Time the prefill step of workload `name` (fixed past lengths, so every step rewrites the
     same rows); optionally follow it with real decode steps at advancing lengths."""
     import torch
@@ -189,13 +190,20 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0):
     past, cache, dev, dr = _layer_setup(dkv, w)
     out = torch.empty((w.B, w.T, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
     ws = torch.empty(dkv.workspace_bytes("prefill", cache, w.B, w.T, w.Hq), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        dkv.attn_prefill(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
-    torch.cuda.synchronize()
-    with EventTimer() as t:
-        for _ in range(steps):
-            dkv.attn_prefill(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
-    res = {"workload": name, "steps": steps, **_prefill_stats(w, past, t.ms / steps, peak_read)}
+    def timed(var, n, nwarm):
+        for _ in range(nwarm):
+            dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
+        torch.cuda.synchronize()
+        with EventTimer() as t:
+            for _ in range(n):
+                dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
+        return t.ms / n
+
+    res = {"workload": name, "steps": steps, "variant": variant,
+           **_prefill_stats(w, past, timed(variant, steps, warmup), peak_read)}
+    if ablations:
+        # the baselines the pages compare the method against, on the same inputs
+        res["ablations_ms"] = {v: timed(v, 2, 1) for v in ablations}
     if decode_steps:
         del out, ws
         xs = [to_dev(dr.normal((w.B, 1, w.D), 1.0, w.dtype), w.dtype) for _ in range(decode_steps)]
@@ -261,6 +269,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_decode_b8_L32768_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", default="fused", choices=["fused", "naive", "separate"],
+                    help="prefill variant for --profile prefill (the ablation baselines)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "calib"],
                     help="short run for rocprofv3: decode steps only, prefill steps only, or the "
@@ -282,7 +292,8 @@ def main():
         calibration_kernels(dkv)
         return
     if args.profile == "prefill":
-        print(json.dumps({"prefill": bench_prefill(dkv, steps=args.steps, warmup=args.warmup)}), flush=True)
+        print(json.dumps({"prefill": run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=args.steps,
+                                                 warmup=args.warmup, variant=args.variant)}), flush=True)
         return
     if args.profile:
         args.no_cpu_baseline = args.no_prefill = True
@@ -351,7 +362,8 @@ def main():
         log("other workloads: tiny fp32 layer")
         tiny = run_prefill(dkv, "tiny_f32_prefill128_decode1", steps=20, warmup=3, peak_read=pr, decode_steps=1)
         log("8B chunked prefill")
-        result["prefill"] = run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=5, warmup=2, peak_read=pr)
+        result["prefill"] = run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=5, warmup=2, peak_read=pr,
+                                        ablations=("naive", "separate"))
         log("long-context fp16 decode")
         longd = run_decode(dkv, "long_decode_b4_L96k_128k_f16", steps=6, warmup=1, peak_read=pr)
         log("70B prefill + 64 decode steps")

@@ -123,6 +123,24 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
                  void* stream);
 
 /*
+ * Ablation baselines for the comparisons the pages report ([N] Experiments & Results:
+ * CPU-aware tiling vs naive zero-copy, Fig. 12; fused vs separate kernels, Fig. 13). Same
+ * arguments, results and errors as attn_prefill; `variant` selects how the host cache is read:
+ *   DKV_PREFILL_FUSED    the attn_prefill path (host KV fetched once per step, new rows kept
+ *                        in device memory);
+ *   DKV_PREFILL_NAIVE    query-stationary tiling pointed at host memory: every query tile
+ *                        streams the whole cache over the link in one launch;
+ *   DKV_PREFILL_SEPARATE projection writes new K/V to the host only, and attention reads
+ *                        them back over the link.
+ * Errors: as attn_prefill, plus INVALID_ARG for an unknown variant.
+ */
+enum { DKV_PREFILL_FUSED = 0, DKV_PREFILL_NAIVE = 1, DKV_PREFILL_SEPARATE = 2 };
+int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                         const void* wv, const int32_t* past_len, int32_t batch, int32_t T,
+                         int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes,
+                         void* stream, int32_t variant);
+
+/*
  * One decode step (T = 1) for every sequence ([N] Attention Fusion Engine, decode
  * strategy): the new token's q, k, v are projected inside the attention kernel, k and v
  * are stored to host row past_len[b], and the query attends to rows 0 .. past_len[b]

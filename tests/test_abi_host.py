@@ -94,6 +94,8 @@ def test_call_validation_statuses(dkv):
     bad = _fake_cache(dkv)
     bad.reserved = 0
     assert L.attn_decode(ctypes.byref(bad), x, w, w, w, lp, 2, 256, 4, out, ws, 1 << 30, None) == -1
+    # unknown prefill variant
+    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, 1 << 30, None, 3) == -1
     assert L.kv_append(None, x, w, w, lp, 2, 1, 256, None) == -1
     # unsupported head_dim / dtype in a descriptor
     assert L.kv_append(ctypes.byref(_fake_cache(dkv, d=96)), x, w, w, lp, 2, 1, 256, None) == -3
@@ -120,8 +122,9 @@ def test_workspace_sizes(dkv):
     lens, lp = _lens([24576])
     ws = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
     e = 2
-    # queries + new K + new V + fp32 running state (o, m, l) per query row
-    want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 8192 * 32 * 130 * 4
+    # queries + new K + new V + fp32 running state: per 32 query rows, 64 lanes x
+    # (d/32 * 16 accumulators + m + l)
+    want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
     assert want <= ws <= want + 4 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
     assert 0 < wsd < (1 << 24)

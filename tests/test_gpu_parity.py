@@ -294,3 +294,24 @@ def test_rejected_calls_enqueue_nothing_and_touch_nothing():
         assert np.array_equal(g.cache.k.view(np.uint8), before.view(np.uint8))
     finally:
         g.free()
+
+
+@pytest.mark.parametrize("variant", ["naive", "separate"])
+def test_prefill_ablation_variants_match_the_oracle(variant):
+    """The baselines the pages compare against compute the same layer step."""
+    import torch
+    from gpu_case import to_dev, torch_dtype
+    case = _case(21, 2, 300, [3000, 4500], 512, 32, 8, 128, "bf16")
+    g = GpuLayer(case, canary=True)
+    try:
+        B, T = case["B"], case["T"]
+        out = torch.empty((B, T, case["Hq"] * case["d"]), dtype=torch_dtype("bf16"), device="cuda")
+        ws = torch.empty(g.dkv.workspace_bytes("prefill", g.cache, B, T, case["Hq"]), dtype=torch.uint8, device="cuda")
+        g.dkv.attn_prefill_variant(g.cache, to_dev(case["x"], "bf16"), g.wq, g.wk, g.wv, case["past_len"],
+                                   case["Hq"], out, ws, variant)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().reshape(B, T, case["Hq"], case["d"])
+    finally:
+        g.free()
+    ref = oracle_step(case, case["x"], case["past_len"], case["kp"].copy(), case["vp"].copy())
+    compare(got, ref, "bf16", f"prefill variant {variant}")

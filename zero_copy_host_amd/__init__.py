@@ -21,7 +21,8 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HOST_ALLOC",
           -5: "HIP", -6: "WORKSPACE"}
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
-           "attn_decode", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+           "attn_prefill_variant", "attn_decode", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2}
 
 
 class DirectKVError(RuntimeError):
@@ -57,12 +58,14 @@ def lib() -> ctypes.CDLL:
         L.attn_workspace_bytes.argtypes = [I32, P(dkv_cache), I32, I32, I32, P(I32)]
         L.attn_workspace_bytes.restype = SZ
         L.attn_prefill.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, I32, VP, VP, SZ, VP]
+        L.attn_prefill_variant.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, I32, VP, VP, SZ,
+                                           VP, I32]
         L.attn_decode.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP]
         L.dkv_hostlink_stream.argtypes = [VP, SZ, I32, I32, VP]
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
-        for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_decode",
-                     "dkv_hostlink_stream"):
+        for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
+                     "attn_decode", "dkv_hostlink_stream"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -157,6 +160,17 @@ def attn_prefill(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, ou
     nbytes = ws.numel() * ws.element_size()
     _check(lib().attn_prefill(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T, D,
                               n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def attn_prefill_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, variant: str,
+                         stream=None) -> None:
+    """attn_prefill with the host cache read as `variant` ("fused", "naive", "separate")."""
+    B, T, D = x.shape
+    lens, lp = _lens(past_len, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().attn_prefill_variant(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T,
+                                      D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream),
+                                      PREFILL_VARIANTS[variant]))
 
 
 def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:

@@ -330,9 +330,18 @@ int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* w
 int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
                  const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads, void* out,
                  void* ws, size_t ws_bytes, void* stream) {
+  return attn_prefill_variant(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes, stream,
+                              DKV_PREFILL_FUSED);
+}
+
+int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                         const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
+                         void* out, void* ws, size_t ws_bytes, void* stream, int32_t variant) {
   int st = check_call(c, batch, T, D, past_len, {x, wq, wk, wv, out});
   if (st) return st;
   if ((st = check_heads(c, n_q_heads))) return st;
+  if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_SEPARATE)
+    return fail(DKV_ERR_INVALID_ARG, "unknown prefill variant %d", variant);
   if (T == 0) return DKV_OK;
   const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads);
   if (!ws || ws_bytes < lay.total || !aligned16(ws))
@@ -349,7 +358,9 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
   float* state = reinterpret_cast<float*>(w + lay.state);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, kn, vn);
+  const bool separate = variant == DKV_PREFILL_SEPARATE;
+  ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
+                          separate ? nullptr : vn);
   hipError_t e = fp(pa, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
 
@@ -369,13 +380,15 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
   aa.cap = c->capacity;
   const int rows = attn_rows_per_tile();
   aa.q_tiles = (T * G + rows - 1) / rows;
-  aa.xcd_group = batch * c->n_kv_heads >= 8;
+  aa.xcd_group = variant != DKV_PREFILL_NAIVE && batch * c->n_kv_heads >= 8;
+  aa.new_from_host = separate;
   int max_keys = 0;
   for (int b = 0; b < batch; ++b) {
     aa.past_len[b] = past_len[b];
     max_keys = std::max(max_keys, past_len[b] + T);
   }
-  const int sk = superchunk_keys(c, batch);
+  // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
+  const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, batch);
   const int nsc = (max_keys + sk - 1) / sk;
   for (int i = 0; i < nsc; ++i) {
     aa.kc0 = i * sk;

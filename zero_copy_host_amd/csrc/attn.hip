@@ -149,8 +149,9 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
         const int kr = c / CPR, kc = (c % CPR) * VEC;
         const int j = j0 + kr;
         if (j < key_hi) {
-          const T* ks = j < L ? kh + (size_t)j * DH : kn + (size_t)(j - L) * DH;
-          const T* vs = j < L ? vh + (size_t)j * DH : vn + (size_t)(j - L) * DH;
+          const bool host = j < L || a.new_from_host;
+          const T* ks = host ? kh + (size_t)j * DH : kn + (size_t)(j - L) * DH;
+          const T* vs = host ? vh + (size_t)j * DH : vn + (size_t)(j - L) * DH;
           rk[i] = *reinterpret_cast<const uint4*>(ks + kc);
           rv[i] = *reinterpret_cast<const uint4*>(vs + kc);
         } else {

@@ -153,6 +153,7 @@ struct AttnArgs {
   int32_t first, last;      // first super-chunk (no state to read) / last (finalise)
   int32_t q_tiles;          // row tiles per (b, g)
   int32_t xcd_group;        // 1: pair p is served only by XCD p % 8 (needs B*Hkv >= 8)
+  int32_t new_from_host;    // 1: this step's rows are read back from the host cache too
   int32_t past_len[kMaxBatch];
 };
 
