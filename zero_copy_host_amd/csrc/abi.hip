@@ -260,6 +260,7 @@ int kv_append(const dkv_cache* c, const void* x, const void* wk, const void* wv,
   proj_fn f = find_proj(c->dtype, c->head_dim);
   if (!f) return fail(DKV_ERR_UNSUPPORTED, "no projection instance for dtype %d head_dim %d", c->dtype, c->head_dim);
   ProjArgs a = make_proj(c, x, nullptr, wk, wv, past_len, batch, T, D, 0, nullptr, nullptr, nullptr);
+  a.host_out = 1;
   hipError_t e = f(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   return DKV_OK;
@@ -361,6 +362,9 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   const bool separate = variant == DKV_PREFILL_SEPARATE;
   ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
                           separate ? nullptr : vn);
+  // the fused path leaves the new rows in device memory here and writes the host copy from
+  // the attention launches, a share each (see attn.hip); the baselines write them from the GEMM
+  pa.host_out = variant != DKV_PREFILL_FUSED;
   hipError_t e = fp(pa, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
 
@@ -395,6 +399,9 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
     aa.kc1 = std::min((i + 1) * sk, max_keys);
     aa.first = i == 0;
     aa.last = i == nsc - 1;
+    aa.store_new = variant == DKV_PREFILL_FUSED;
+    aa.store_part = i;
+    aa.store_parts = nsc;
     e = fa(aa, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }

@@ -73,9 +73,32 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
 
+  const int P = a.B * a.Hkv;
+  if (a.store_new) {
+    // storer role: this step's new K/V rows go from their device copy to the host cache.
+    // The link's write direction is otherwise idle during attention (its host traffic is
+    // reads), so the writes overlap the reads. Launch i of n copies rows
+    // [i*rows/n, (i+1)*rows/n); every workgroup copies its share before any early exit.
+    const int rows = P * a.T;                          // (pair, token) rows, d elements each
+    const int lr0 = (int)((long long)rows * a.store_part / a.store_parts);
+    const int lr1 = (int)((long long)rows * (a.store_part + 1) / a.store_parts);
+    const int per = (lr1 - lr0 + gridDim.x - 1) / gridDim.x;
+    const int r0 = lr0 + blockIdx.x * per, r1 = min(r0 + per, lr1);
+    constexpr int CPR = DH / C::VEC;
+    for (int c = r0 * CPR + (int)threadIdx.x; c < r1 * CPR; c += C::THREADS) {
+      const int row = c / CPR, col = (c - row * CPR) * C::VEC;
+      const int pp = row / a.T, t = row - pp * a.T;
+      const int bb = pp / a.Hkv;
+      const size_t src = ((size_t)pp * a.T + t) * DH + col;
+      const size_t dst = ((size_t)pp * a.cap + a.past_len[bb] + t) * DH + col;
+      const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.k_new) + src);
+      const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.v_new) + src);
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.kc)) + dst) = kv;
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.vc)) + dst) = vv;
+    }
+  }
   // workgroup -> (sequence/kv-head pair p, query tile qt). With at least 8 pairs, pair p is
   // served only by XCD p % 8 (workgroup i runs on XCD i % 8).
-  const int P = a.B * a.Hkv;
   int p, qt;
   if (a.xcd_group) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;

@@ -114,6 +114,7 @@ struct ProjArgs {
   void* vc;                 // host cache V (segment 2)
   void* k_dev;              // optional device copy of the new K rows [B, Hkv, T, d]
   void* v_dev;              // optional device copy of the new V rows
+  int32_t host_out;         // 1: write the new K/V rows to the host cache (segments 1, 2)
   int32_t past_len[kMaxBatch];
 };
 
@@ -154,6 +155,8 @@ struct AttnArgs {
   int32_t q_tiles;          // row tiles per (b, g)
   int32_t xcd_group;        // 1: pair p is served only by XCD p % 8 (needs B*Hkv >= 8)
   int32_t new_from_host;    // 1: this step's rows are read back from the host cache too
+  int32_t store_new;        // 1: also copy this step's rows from k_new/v_new to the host cache
+  int32_t store_part, store_parts;  // this launch copies share store_part of store_parts
   int32_t past_len[kMaxBatch];
 };
 

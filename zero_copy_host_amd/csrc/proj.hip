@@ -4,22 +4,28 @@
 // Follows "Paper Notes: DirectKV", Fundamental Underlying Technologies / Kernel Fusion
 // (K = X·Wk, V = X·Wv) and System Architecture / KV Cache Manager: the K and V rows go
 // straight into the pinned host cache at rows [past_len[b], past_len[b] + T) (the storer
-// role); Q goes to device memory, where the pages keep the queries. Optionally the new
-// K/V rows are also left in device memory, so that attention over them never reads them
-// back across the host link.
+// role); Q goes to device memory, where the pages keep the queries. The new K/V rows can
+// also (or only) be left in device memory, so that attention over them never reads them
+// back across the host link; in a fused prefill the host copy is then written by the first
+// attention launch, whose link traffic is otherwise all in the read direction.
 //
 // gfx950 mapping: 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, each
-// wave 2x2 blocks of the 32x32 MFMA; K steps of 32 through a double-buffered LDS tile
+// wave 2x2 blocks of the 32x32 MFMA; K steps of 64 through a double-buffered LDS tile
 // (X and W both stored k-contiguous, padded by 16 bytes per row against bank conflicts).
+// The reduction depth per stage (64) needs D % 64 == 0, which the ABI checks.
 // The epilogue is staged through LDS so every output row leaves as full 16-byte-per-lane
 // contiguous writes (whole host cache lines for K and V).
 #include "dkv_internal.h"
 
 namespace dkv {
 
+#ifndef DKV_PROJ_BK
+#define DKV_PROJ_BK 64   // reduction depth per LDS stage (build-time tunable)
+#endif
+
 template <typename T>
 struct ProjCfg {
-  static constexpr int BM = 128, BN = 128, BK = 32;
+  static constexpr int BM = 128, BN = 128, BK = DKV_PROJ_BK;
   static constexpr int EB = sizeof(T);
   static constexpr int VEC = 16 / EB;            // elements per 16-byte chunk
   static constexpr int LDK = BK + VEC;           // padded row length in LDS (elements)
@@ -45,9 +51,13 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // which segment and column tile this workgroup owns
-  int seg = 0, ty = blockIdx.y;
-  while (seg < 2 && ty >= a.tiles_seg[seg]) { ty -= a.tiles_seg[seg]; ++seg; }
+  // which segment and column tile this workgroup owns. The K and V tiles, whose epilogue
+  // writes go over the host link, are dispatched first so that those posted writes drain
+  // while the Q tiles (device memory only) are still computing.
+  constexpr int order[3] = {1, 2, 0};
+  int oi = 0, ty = blockIdx.y;
+  while (oi < 2 && ty >= a.tiles_seg[order[oi]]) { ty -= a.tiles_seg[order[oi]]; ++oi; }
+  const int seg = order[oi];
   const int n0 = ty * BN;
   const int nseg = a.n_seg[seg];
   const int m0 = blockIdx.x * BM;
@@ -138,8 +148,10 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
       const int b = m / a.T, t = m - b * a.T;
       const int gg = n / a.d, i = n - gg * a.d;
       const size_t bgk = (size_t)b * a.Hkv + gg;
-      T* cache = reinterpret_cast<T*>(seg == 1 ? a.kc : a.vc);
-      *reinterpret_cast<uint4*>(cache + (bgk * a.cap + a.past_len[b] + t) * a.d + i) = val;
+      if (a.host_out) {
+        T* cache = reinterpret_cast<T*>(seg == 1 ? a.kc : a.vc);
+        *reinterpret_cast<uint4*>(cache + (bgk * a.cap + a.past_len[b] + t) * a.d + i) = val;
+      }
       void* dev = seg == 1 ? a.k_dev : a.v_dev;
       if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
     }
