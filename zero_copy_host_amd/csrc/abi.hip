@@ -169,6 +169,18 @@ int superchunk_keys(const dkv_cache* c, int32_t batch) {
   return (int)std::min<size_t>(keys, 1 << 20);
 }
 
+// Keys of [k0, k1) visible to the T new tokens of a sequence with past length L (token t
+// sees keys 0 .. L + t), summed over the tokens: the attention work of one super-chunk.
+long long visible_keys(int L, int T, int k0, int k1) {
+  auto sum_pos = [T](long long c) {   // sum over t in [0, T) of max(c + t, 0)
+    const long long t0 = std::max(0LL, 1 - c);
+    if (t0 >= T) return 0LL;
+    return (T - t0) * (2 * c + t0 + T - 1) / 2;
+  };
+  const long long c = (long long)L + 1 - k0;   // token t sees c + t keys of the range, unclamped
+  return sum_pos(c) - sum_pos(c - (k1 - k0));
+}
+
 ProjArgs make_proj(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
                    const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
                    void* q_out, void* k_dev, void* v_dev) {
@@ -363,7 +375,7 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
                           separate ? nullptr : vn);
   // the fused path leaves the new rows in device memory here and writes the host copy from
-  // the attention launches, a share each (see attn.hip); the baselines write them from the GEMM
+  // attention launches (see below and attn.hip); the baselines write them from the GEMM
   pa.host_out = variant != DKV_PREFILL_FUSED;
   hipError_t e = fp(pa, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
@@ -394,14 +406,41 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
   const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, batch);
   const int nsc = (max_keys + sk - 1) / sk;
+  // The new rows' host copies are written by launches whose keys hold no host rows (no
+  // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
+  // super-chunk from L2; with no such launch, the last one writes them all. The rows are
+  // split among those launches in proportion to their attention work.
+  int max_past = 0;
+  for (int b = 0; b < batch; ++b) max_past = std::max(max_past, past_len[b]);
+  int first_free = nsc - 1;
+  for (int i = 0; i < nsc; ++i)
+    if (i * sk >= max_past) { first_free = i; break; }
+  auto launch_work = [&](int i) {
+    long long w = 0;
+    for (int b = 0; b < batch; ++b) w += visible_keys(past_len[b], T, i * sk, std::min((i + 1) * sk, max_keys));
+    return w;
+  };
+  long long work_total = 0;
+  for (int i = first_free; i < nsc; ++i) work_total += launch_work(i);
+  const long long new_rows = (long long)batch * c->n_kv_heads * T;
+  long long work_before = 0;
   for (int i = 0; i < nsc; ++i) {
     aa.kc0 = i * sk;
     aa.kc1 = std::min((i + 1) * sk, max_keys);
     aa.first = i == 0;
     aa.last = i == nsc - 1;
-    aa.store_new = variant == DKV_PREFILL_FUSED;
-    aa.store_part = i;
-    aa.store_parts = nsc;
+    aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
+    if (aa.store_new) {
+      const long long w = launch_work(i);
+      if (work_total > 0) {
+        aa.store_lo = (int)(new_rows * work_before / work_total);
+        aa.store_hi = (int)(new_rows * (work_before + w) / work_total);
+      } else {
+        aa.store_lo = (int)(new_rows * (i - first_free) / (nsc - first_free));
+        aa.store_hi = (int)(new_rows * (i - first_free + 1) / (nsc - first_free));
+      }
+      work_before += w;
+    }
     e = fa(aa, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }

@@ -70,20 +70,19 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T sK[2][C::KTILE];
   __shared__ __attribute__((aligned(16))) T sV[2][C::VTILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int half = lane >> 5, col = lane & 31;
 
   const int P = a.B * a.Hkv;
   if (a.store_new) {
     // storer role: this step's new K/V rows go from their device copy to the host cache.
-    // The link's write direction is otherwise idle during attention (its host traffic is
-    // reads), so the writes overlap the reads. Launch i of n copies rows
-    // [i*rows/n, (i+1)*rows/n); every workgroup copies its share before any early exit.
-    const int rows = P * a.T;                          // (pair, token) rows, d elements each
-    const int lr0 = (int)((long long)rows * a.store_part / a.store_parts);
-    const int lr1 = (int)((long long)rows * (a.store_part + 1) / a.store_parts);
-    const int per = (lr1 - lr0 + gridDim.x - 1) / gridDim.x;
-    const int r0 = lr0 + blockIdx.x * per, r1 = min(r0 + per, lr1);
+    // The host hands each storing launch a share of the (pair, token) rows, [store_lo,
+    // store_hi), split among the launches that hold no host rows (so the writes cannot evict
+    // a resident super-chunk from L2) in proportion to their attention work, so the writes
+    // drain under their compute. Every workgroup copies its part before any early exit.
+    const int per = (a.store_hi - a.store_lo + gridDim.x - 1) / gridDim.x;
+    const int r0 = a.store_lo + blockIdx.x * per, r1 = min(r0 + per, a.store_hi);
     constexpr int CPR = DH / C::VEC;
     for (int c = r0 * CPR + (int)threadIdx.x; c < r1 * CPR; c += C::THREADS) {
       const int row = c / CPR, col = (c - row * CPR) * C::VEC;
@@ -98,17 +97,18 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
     }
   }
   // workgroup -> (sequence/kv-head pair p, query tile qt). With at least 8 pairs, pair p is
-  // served only by XCD p % 8 (workgroup i runs on XCD i % 8).
+  // served only by XCD p % 8 (workgroup i runs on XCD i % 8). Query tiles go out last row
+  // first: under the causal mask later rows see more keys, so the longest tiles start first.
   int p, qt;
   if (a.xcd_group) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int ppx = (P + 7) >> 3;
     p = (slot % ppx) * 8 + xcd;
-    qt = slot / ppx;
+    qt = a.q_tiles - 1 - slot / ppx;
     if (p >= P) return;
   } else {
     p = blockIdx.x % P;
-    qt = blockIdx.x / P;
+    qt = a.q_tiles - 1 - blockIdx.x / P;
   }
   const int b = p / a.Hkv, g = p - b * a.Hkv;
   const int L = a.past_len[b];
@@ -164,30 +164,49 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
     const T* __restrict__ kn = reinterpret_cast<const T*>(a.k_new) + bg * a.T * DH;
     const T* __restrict__ vn = reinterpret_cast<const T*>(a.v_new) + bg * a.T * DH;
 
+    const int host_end = a.new_from_host ? key_hi : L;   // keys below this come from the host
+    // this thread's 16-byte chunks of a tile: chunk i is key row krow[i], element offset off[i]
+    int krow[LOADS], off[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + i * C::THREADS;
+      krow[i] = c / CPR;
+      off[i] = krow[i] * DH + (c % CPR) * VEC;
+    }
     uint4 rk[LOADS], rv[LOADS];
     auto gload = [&](int j0) {
+      if (j0 + KT <= key_hi && (j0 + KT <= host_end || j0 >= host_end)) {
+        // whole tile from one source: one uniform base, per-lane offsets
+        const bool host = j0 + KT <= host_end;
+        const T* kb0 = host ? kh + (size_t)j0 * DH : kn + (size_t)(j0 - L) * DH;
+        const T* vb0 = host ? vh + (size_t)j0 * DH : vn + (size_t)(j0 - L) * DH;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int c = tid + i * C::THREADS;
-        const int kr = c / CPR, kc = (c % CPR) * VEC;
-        const int j = j0 + kr;
-        if (j < key_hi) {
-          const bool host = j < L || a.new_from_host;
-          const T* ks = host ? kh + (size_t)j * DH : kn + (size_t)(j - L) * DH;
-          const T* vs = host ? vh + (size_t)j * DH : vn + (size_t)(j - L) * DH;
-          rk[i] = *reinterpret_cast<const uint4*>(ks + kc);
-          rv[i] = *reinterpret_cast<const uint4*>(vs + kc);
-        } else {
-          rk[i] = make_uint4(0, 0, 0, 0);
-          rv[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < LOADS; ++i) {
+          rk[i] = *reinterpret_cast<const uint4*>(kb0 + off[i]);
+          rv[i] = *reinterpret_cast<const uint4*>(vb0 + off[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int j = j0 + krow[i];
+          const int e = off[i] - krow[i] * DH;
+          if (j < key_hi) {
+            const bool host = j < host_end;
+            const T* ks = host ? kh + (size_t)j * DH : kn + (size_t)(j - L) * DH;
+            const T* vs = host ? vh + (size_t)j * DH : vn + (size_t)(j - L) * DH;
+            rk[i] = *reinterpret_cast<const uint4*>(ks + e);
+            rv[i] = *reinterpret_cast<const uint4*>(vs + e);
+          } else {
+            rk[i] = make_uint4(0, 0, 0, 0);
+            rv[i] = make_uint4(0, 0, 0, 0);
+          }
         }
       }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int c = tid + i * C::THREADS;
-        const int kr = c / CPR, kc = (c % CPR) * VEC;
+        const int kr = krow[i], kc = off[i] - kr * DH;
         *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = rk[i];
         if constexpr (C::VROW) {
           *reinterpret_cast<uint4*>(&sV[buf][kr * LDV + kc]) = rv[i];

@@ -156,7 +156,7 @@ struct AttnArgs {
   int32_t xcd_group;        // 1: pair p is served only by XCD p % 8 (needs B*Hkv >= 8)
   int32_t new_from_host;    // 1: this step's rows are read back from the host cache too
   int32_t store_new;        // 1: also copy this step's rows from k_new/v_new to the host cache
-  int32_t store_part, store_parts;  // this launch copies share store_part of store_parts
+  int32_t store_lo, store_hi;  // (pair, token) rows [store_lo, store_hi) this launch copies
   int32_t past_len[kMaxBatch];
 };
 
