@@ -240,6 +240,67 @@ def run_decode(dkv, name, steps=10, warmup=2, peak_read=None):
             **_decode_stats(w, past, t.ms / steps, peak_read)}
 
 
+def _paged_copy(dkv, w, past, cache, seed):
+    """A page pool holding the rows of a filled contiguous cache through a shuffled block table
+    (each sequence gets the pages this step needs, in random physical order)."""
+    need = [(int(L) + w.T + dkv.PAGE_TOKENS - 1) // dkv.PAGE_TOKENS for L in past]
+    total = sum(need)
+    pool = dkv.PagedHostKVCache(total, w.Hkv, w.d, w.dtype)
+    perm = np.random.default_rng(seed).permutation(total)
+    lists, off = [], 0
+    for n in need:
+        lists.append(perm[off:off + n].tolist())
+        off += n
+    table = dkv.block_table(lists, max(need))
+    for b, n in enumerate(need):
+        rows = n * dkv.PAGE_TOKENS
+        for src, dst in ((cache.k, pool.k), (cache.v, pool.v)):
+            dst[table[b, :n]] = src[b, :, :rows].reshape(w.Hkv, n, dkv.PAGE_TOKENS, w.d).transpose(1, 0, 2, 3)
+    return pool, table
+
+
+def run_paged(dkv, peak_read=None, decode_steps=10, prefill_steps=3):
+    """The 8B decode step and the 8B chunked prefill on a paged host cache (16-token pages in
+    shuffled physical order), beside the contiguous numbers."""
+    import torch
+    import synth
+    res = {}
+    w = synth.workload("llama8b_decode_b8_L32768_bf16")
+    past, cache, dev, _ = _layer_setup(dkv, w)
+    pool, table = _paged_copy(dkv, w, past, cache, w.seed)
+    cache.free()
+    out = torch.empty((w.B, 1, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    ws = torch.empty(dkv.paged_workspace_bytes("decode", pool, w.B, 1, w.Hq, table.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(2):
+        dkv.attn_decode_paged(pool, table, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for _ in range(decode_steps):
+            dkv.attn_decode_paged(pool, table, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    res["decode"] = {"workload": w.name, "steps": decode_steps, "pages": pool.n_pages,
+                     **_decode_stats(w, past, t.ms / decode_steps, peak_read)}
+    pool.free()
+    del out, ws
+
+    w = synth.workload("llama8b_prefill_T8192_on_L24576_bf16")
+    past, cache, dev, _ = _layer_setup(dkv, w)
+    pool, table = _paged_copy(dkv, w, past, cache, w.seed)
+    cache.free()
+    out = torch.empty((w.B, w.T, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    ws = torch.empty(dkv.paged_workspace_bytes("prefill", pool, w.B, w.T, w.Hq, table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    dkv.attn_prefill_paged(pool, table, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for _ in range(prefill_steps):
+            dkv.attn_prefill_paged(pool, table, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    res["prefill"] = {"workload": w.name, "steps": prefill_steps, "pages": pool.n_pages,
+                      **_prefill_stats(w, past, t.ms / prefill_steps, peak_read)}
+    pool.free()
+    return res
+
+
 def bench_prefill(dkv, steps=5, warmup=2):
     return run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps, warmup)
 
@@ -272,8 +333,9 @@ def main():
     ap.add_argument("--variant", default="fused", choices=["fused", "naive", "separate"],
                     help="prefill variant for --profile prefill (the ablation baselines)")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "calib"],
-                    help="short run for rocprofv3: decode steps only, prefill steps only, or the "
+    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "paged", "calib"],
+                    help="short run for rocprofv3: decode steps only, prefill steps only, the paged-cache "
+                         "decode and prefill, or the "
                          "counter calibration kernels (1 GiB host read, 1 GiB host write, 1 GiB "
                          "device-to-device copy)")
     args = ap.parse_args()
@@ -290,6 +352,10 @@ def main():
 
     if args.profile == "calib":
         calibration_kernels(dkv)
+        return
+    if args.profile == "paged":
+        print(json.dumps({"paged": run_paged(dkv, decode_steps=args.steps, prefill_steps=max(1, args.steps // 3))}),
+              flush=True)
         return
     if args.profile == "prefill":
         print(json.dumps({"prefill": run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=args.steps,
@@ -369,6 +435,8 @@ def main():
         log("70B prefill + 64 decode steps")
         big = run_prefill(dkv, "llama70b_prefill_T16384_on_L49152_b2_bf16", steps=2, warmup=1, peak_read=pr,
                           decode_steps=64)
+        log("paged host cache: 8B decode and 8B chunked prefill")
+        result["paged"] = run_paged(dkv, peak_read=pr)
         result["workloads"] = {"tiny_f32_prefill128_decode1": tiny,
                                "llama8b_prefill_T8192_on_L24576_bf16": result["prefill"],
                                "long_decode_b4_L96k_128k_f16": longd,

@@ -152,6 +152,69 @@ int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* w
                 int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- Paged host cache ([N] KV Cache Manager; the page manager of the pages' reference
+ * simulator: 16-token pages of pinned host memory, a table from a sequence's logical pages to
+ * physical pages, no device staging buffer).
+ *
+ * A pool of n_pages pages in pinned, mapped host memory. k and v are each
+ * [n_pages][n_kv_heads][DKV_PAGE_TOKENS][head_dim] row-major: one page holds 16 consecutive
+ * tokens of every kv head, and the 16 rows of one (page, head) are contiguous. Which pages a
+ * sequence uses is the caller's business: a block table, a host array of int32
+ * [batch][max_pages] row-major, names for logical page p of sequence b (tokens
+ * [16p, 16p + 16)) its physical page block_table[b * max_pages + p]. Several sequences may
+ * map the same page for reading (a shared prefix); a page a call writes must be mapped once.
+ *
+ * The paged calls compute exactly what the contiguous ones do on the gathered cache. They
+ * read the block table during the call (it may be changed after they return), check every
+ * entry they use on the host (page ids in [0, n_pages); pages written by the call mapped only
+ * once among the used entries; past_len[b] + T <= 16 * max_pages, else CAPACITY), and copy it
+ * to the front of the workspace, which therefore also covers batch * max_pages int32 values.
+ */
+#define DKV_PAGE_TOKENS 16
+
+typedef struct dkv_paged_cache {
+  void* k;
+  void* v;
+  int32_t n_pages;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* a dkv_dtype */
+  int32_t reserved;
+  int32_t pad;
+} dkv_paged_cache;
+
+/* Allocate the K and V page pools with hipHostMalloc (mapped, coherent); no device memory.
+ * Contents are undefined. Errors: INVALID_ARG, UNSUPPORTED (head_dim, dtype), HOST_ALLOC. */
+int kv_paged_alloc_host(dkv_paged_cache* out, int32_t n_pages, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t dtype);
+
+/* Free both pools and zero the descriptor. Idempotent. */
+int kv_paged_free_host(dkv_paged_cache* c);
+
+/* Device workspace of a paged call, in bytes: phase 0 prefill (T tokens), 1 decode, 2
+ * append. Covers the block table copy plus what the contiguous call needs. 0 on bad input. */
+size_t attn_paged_workspace_bytes(int32_t phase, const dkv_paged_cache* c, int32_t batch, int32_t T,
+                                  int32_t n_q_heads, int32_t max_pages);
+
+/* kv_append on a paged cache: token L_b + t of head g goes to row (L_b + t) % 16 of page
+ * block_table[b][(L_b + t) / 16]. No other row is written. */
+int kv_paged_append(const dkv_paged_cache* c, const int32_t* block_table, int32_t max_pages, const void* x,
+                    const void* wk, const void* wv, const int32_t* past_len, int32_t batch, int32_t T,
+                    int32_t D, void* ws, size_t ws_bytes, void* stream);
+
+/* attn_prefill on a paged cache (the fused path). */
+int attn_prefill_paged(const dkv_paged_cache* c, const int32_t* block_table, int32_t max_pages,
+                       const void* x, const void* wq, const void* wk, const void* wv,
+                       const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
+                       void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* attn_decode on a paged cache. */
+int attn_decode_paged(const dkv_paged_cache* c, const int32_t* block_table, int32_t max_pages,
+                      const void* x, const void* wq, const void* wk, const void* wv,
+                      const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Streaming read (mode 0) or write (mode 1) of `bytes` bytes of pinned host memory at
  * `host_ptr` by a kernel, the same access path the attention kernels use; measures the
  * host-link rate the layer is bounded by. bytes must be a multiple of 16 * n_wg;

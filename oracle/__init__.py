@@ -30,6 +30,12 @@ Where the pages leave a step open, the readings taken are:
 
 Arrays: X [B, T, D]; Wq [D, Hq·d]; Wk, Wv [D, Hkv·d]; caches [B, Hkv, cap, d]
 (float32 arrays whose values are exact in the cache dtype, or fp64); past_len int [B].
+
+A paged cache (16-token pages and a table from a sequence's logical pages to physical
+pages — "DirectKV Guide: Zero-Copy KV Offloading on GH200 & GB200", section "End-to-End
+Implementation: Building DirectKV in Python", its memory configuration and page manager)
+holds the same logical cache: gather_pages gives it back, and the layer step on a paged
+cache is the layer step above on the gathered cache.
 """
 from __future__ import annotations
 
@@ -127,3 +133,27 @@ def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads: int, dtype: str, t_in
     ts = np.arange(T) if t_index is None else np.asarray(t_index, dtype=np.int64)
     q = project(x[:, ts, :], wq).reshape(B, len(ts), n_q_heads, d)
     return attention(q, kc, vc, past_len, ts)
+
+
+PAGE_TOKENS = 16   # tokens per page of a paged cache (the page manager's page size)
+
+
+def gather_pages(pool, table, n_tokens) -> np.ndarray:
+    """The logical cache held by a paged pool.
+
+    pool [n_pages, H, 16, d]; table int [B, max_pages] (logical page p of sequence b is
+    physical page table[b, p]); n_tokens int [B]. Returns fp64 [B, H, max(n_tokens), d]:
+    row j < n_tokens[b] of (sequence b, head g) is pool[table[b, j // 16], g, j % 16];
+    rows at or past n_tokens[b] are NaN."""
+    pool = np.asarray(pool, dtype=np.float64)
+    table = np.asarray(table)
+    B = table.shape[0]
+    H, d = pool.shape[1], pool.shape[3]
+    n = int(max(n_tokens)) if B else 0
+    out = np.full((B, H, n, d), np.nan)
+    for b in range(B):
+        j = np.arange(int(n_tokens[b]))
+        rows = pool[table[b, j // PAGE_TOKENS], :, j % PAGE_TOKENS, :]   # [len(j), H, d]
+        out[b, :, : len(j), :] = rows.transpose(1, 0, 2)
+    return out
+

@@ -130,3 +130,77 @@ def test_workspace_sizes(dkv):
     assert 0 < wsd < (1 << 24)
     assert L.attn_workspace_bytes(2, ctypes.byref(c), 1, 1, 32, lp) == 0
     assert L.attn_workspace_bytes(1, None, 1, 1, 32, lp) == 0
+
+
+# ---- paged cache: the block table is checked on the host before anything is enqueued
+
+PAGED_MAGIC = 0x444B5650   # the mark kv_paged_alloc_host leaves in a descriptor
+
+
+def _fake_paged(dkv, n_pages=8, Hkv=2, d=128, dtype=2):
+    c = dkv.dkv_paged_cache()
+    c.k, c.v = 0x1000, 0x2000          # never dereferenced: every call below stops before a launch
+    c.n_pages, c.n_kv_heads, c.head_dim, c.dtype, c.reserved = n_pages, Hkv, d, dtype, PAGED_MAGIC
+    return c
+
+
+def _tab(rows):
+    t = np.ascontiguousarray(np.array(rows, dtype=np.int32))
+    return t, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), t.shape[1]
+
+
+def test_paged_table_validation(dkv):
+    L = dkv.lib()
+    c = _fake_paged(dkv)
+    x = w = out = ws = 0x10000
+    big = 1 << 30
+    lens, lp = _lens([20, 3])                       # sequence 0 uses pages 0-1, sequence 1 page 0
+    ok, okp, mp = _tab([[4, 5, -1], [6, -1, -1]])
+    # a valid table gets through every check; T = 0 then returns before any copy or launch
+    assert L.attn_prefill_paged(ctypes.byref(c), okp, mp, x, w, w, w, lp, 2, 0, 256, 8, out, ws, big, None) == 0
+    # page id outside the pool
+    bad, badp, _ = _tab([[4, 9, -1], [6, -1, -1]])
+    assert L.attn_decode_paged(ctypes.byref(c), badp, mp, x, w, w, w, lp, 2, 256, 8, out, ws, big, None) == -1
+    assert "outside" in _err(dkv)
+    # an unused entry (-1) beyond the used pages is fine; a used -1 is not
+    bad, badp, _ = _tab([[4, -1, -1], [6, -1, -1]])
+    assert L.attn_decode_paged(ctypes.byref(c), badp, mp, x, w, w, w, lp, 2, 256, 8, out, ws, big, None) == -1
+    # the page a call writes may not be mapped twice (sequence 1 writes token 3 on page 4,
+    # which sequence 0 also reads)
+    bad, badp, _ = _tab([[4, 5, -1], [4, -1, -1]])
+    assert L.attn_decode_paged(ctypes.byref(c), badp, mp, x, w, w, w, lp, 2, 256, 8, out, ws, big, None) == -1
+    assert "mapped 2 times" in _err(dkv)
+    # shared pages that nobody writes are fine: both read page 4, sequence 1 writes page 7
+    lens2, lp2 = _lens([20, 16])
+    sh, shp, _ = _tab([[4, 5, -1], [4, 7, -1]])
+    assert L.attn_prefill_paged(ctypes.byref(c), shp, mp, x, w, w, w, lp2, 2, 0, 256, 8, out, ws, big, None) == 0
+    # capacity: 3 pages hold 48 tokens
+    lens3, lp3 = _lens([47, 0])
+    assert L.attn_decode_paged(ctypes.byref(c), okp, mp, x, w, w, w, lp3, 2, 256, 8, out, ws, big, None) in (-1, -2)
+    lens4, lp4 = _lens([48, 0])
+    full, fullp, _ = _tab([[0, 1, 2], [3, -1, -1]])
+    assert L.attn_decode_paged(ctypes.byref(c), fullp, mp, x, w, w, w, lp4, 2, 256, 8, out, ws, big, None) == -2
+    # workspace too small, null table, descriptor not from kv_paged_alloc_host
+    assert L.attn_decode_paged(ctypes.byref(c), okp, mp, x, w, w, w, lp, 2, 256, 8, out, ws, 64, None) == -6
+    assert L.kv_paged_append(ctypes.byref(c), okp, mp, x, w, w, lp, 2, 1, 256, ws, 16, None) == -6
+    assert L.attn_decode_paged(ctypes.byref(c), None, mp, x, w, w, w, lp, 2, 256, 8, out, ws, big, None) == -1
+    nd = _fake_paged(dkv)
+    nd.reserved = MAGIC                              # a contiguous descriptor's mark
+    assert L.attn_decode_paged(ctypes.byref(nd), okp, mp, x, w, w, w, lp, 2, 256, 8, out, ws, big, None) == -1
+
+
+def test_paged_workspace_sizes(dkv):
+    L = dkv.lib()
+    c = _fake_paged(dkv, n_pages=4096, Hkv=8)
+    cc = _fake_cache(dkv, B=2, Hkv=8, d=128, cap=64 * 16)
+    lens, lp = _lens([500, 900])
+    table_bytes = ((2 * 64 * 4 + 255) // 256) * 256
+    assert L.attn_paged_workspace_bytes(2, ctypes.byref(c), 2, 1, 32, 64) == table_bytes
+    # prefill: the table plus exactly what the contiguous call needs
+    assert (L.attn_paged_workspace_bytes(0, ctypes.byref(c), 2, 128, 32, 64)
+            == table_bytes + L.attn_workspace_bytes(0, ctypes.byref(cc), 2, 128, 32, lp))
+    # decode: the table plus at least the contiguous partials
+    assert (L.attn_paged_workspace_bytes(1, ctypes.byref(c), 2, 1, 32, 64)
+            >= table_bytes + L.attn_workspace_bytes(1, ctypes.byref(cc), 2, 1, 32, lp))
+    assert L.attn_paged_workspace_bytes(1, None, 2, 1, 32, 64) == 0
+    assert L.attn_paged_workspace_bytes(1, ctypes.byref(c), 2, 1, 32, 0) == 0

@@ -338,3 +338,62 @@ def test_empty_step_returns_nothing():
     out = oracle.layer_step(x, wq, wk, wv, kc, vc, past, 2, "f32")
     assert out.shape == (1, 0, 2, 4)
     assert np.array_equal(before, kc)
+
+
+# ---- paged cache: gather_pages is the block-table mapping, pinned by construction and loops
+
+def test_gather_pages_of_an_in_order_pool_is_the_contiguous_cache():
+    # a contiguous cache cut into 16-row pages in order, table = identity
+    rng = np.random.default_rng(40)
+    H, d, n_pages = 3, 4, 5
+    cache = rng.standard_normal((1, H, 16 * n_pages, d))
+    pool = np.zeros((n_pages, H, 16, d))
+    for p in range(n_pages):
+        for g in range(H):
+            for r in range(16):
+                pool[p, g, r] = cache[0, g, 16 * p + r]
+    got = oracle.gather_pages(pool, np.arange(n_pages)[None, :], [16 * n_pages])
+    assert np.array_equal(got, cache)
+
+
+def test_gather_pages_matches_loops_on_a_shuffled_table():
+    rng = np.random.default_rng(41)
+    H, d, n_pages, B, max_pages = 2, 3, 11, 3, 4
+    pool = rng.standard_normal((n_pages, H, 16, d))
+    perm = rng.permutation(n_pages)
+    table = perm[: B * max_pages - 1].tolist() + [perm[0]]     # one page shared (read-only)
+    table = np.array(table).reshape(B, max_pages)
+    n_tokens = [37, 64, 1]
+    got = oracle.gather_pages(pool, table, n_tokens)
+    assert got.shape == (B, H, 64, d)
+    for b in range(B):
+        for g in range(H):
+            for j in range(64):
+                if j < n_tokens[b]:
+                    page, row = table[b][j // 16], j % 16
+                    assert np.array_equal(got[b, g, j], pool[page, g, row])
+                else:
+                    assert np.isnan(got[b, g, j]).all()
+
+
+def test_paged_layer_step_equals_contiguous_layer_step():
+    # the same logical cache as pages or contiguous gives the same layer step
+    x, wq, wk, wv, kc, vc, past = _random_layer(42, 2, 3, [20, 33], 8, 4, 2, 4, "bf16")
+    B, Hkv, cap, d = kc.shape
+    n_lp = (cap + 15) // 16
+    rng = np.random.default_rng(43)
+    perm = rng.permutation(B * n_lp)
+    table = perm.reshape(B, n_lp)
+    pool_k = np.full((B * n_lp, Hkv, 16, d), np.nan)
+    pool_v = np.full((B * n_lp, Hkv, 16, d), np.nan)
+    for b in range(B):
+        for j in range(cap):
+            pool_k[table[b, j // 16], :, j % 16] = kc[b, :, j]
+            pool_v[table[b, j // 16], :, j % 16] = vc[b, :, j]
+    want = oracle.layer_step(x, wq, wk, wv, kc, vc, past, 4, "bf16")
+    n_tok = [int(p) + 3 for p in past]
+    kg = oracle.gather_pages(pool_k, table, [cap, cap])
+    vg = oracle.gather_pages(pool_v, table, [cap, cap])
+    got = oracle.layer_step(x, wq, wk, wv, kg, vg, past, 4, "bf16")
+    assert np.array_equal(got, want)
+    assert max(n_tok) <= cap

@@ -21,7 +21,10 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HOST_ALLOC",
           -5: "HIP", -6: "WORKSPACE"}
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
-           "attn_prefill_variant", "attn_decode", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+           "attn_prefill_variant", "attn_decode", "kv_paged_alloc_host", "kv_paged_free_host",
+           "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
+           "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+PAGE_TOKENS = 16
 PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2}
 
 
@@ -35,6 +38,12 @@ class dkv_cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("batch", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class dkv_paged_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n_pages", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,11 +70,21 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_variant.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, I32, VP, VP, SZ,
                                            VP, I32]
         L.attn_decode.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP]
+        L.kv_paged_alloc_host.argtypes = [P(dkv_paged_cache), I32, I32, I32, I32]
+        L.kv_paged_free_host.argtypes = [P(dkv_paged_cache)]
+        L.attn_paged_workspace_bytes.argtypes = [I32, P(dkv_paged_cache), I32, I32, I32, I32]
+        L.attn_paged_workspace_bytes.restype = SZ
+        L.kv_paged_append.argtypes = [P(dkv_paged_cache), P(I32), I32, VP, VP, VP, P(I32), I32, I32, I32, VP, SZ, VP]
+        L.attn_prefill_paged.argtypes = [P(dkv_paged_cache), P(I32), I32, VP, VP, VP, VP, P(I32), I32, I32, I32,
+                                         I32, VP, VP, SZ, VP]
+        L.attn_decode_paged.argtypes = [P(dkv_paged_cache), P(I32), I32, VP, VP, VP, VP, P(I32), I32, I32, I32,
+                                        VP, VP, SZ, VP]
         L.dkv_hostlink_stream.argtypes = [VP, SZ, I32, I32, VP]
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
         for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
-                     "attn_decode", "dkv_hostlink_stream"):
+                     "attn_decode", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
+                     "attn_prefill_paged", "attn_decode_paged", "dkv_hostlink_stream"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -180,6 +199,121 @@ def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out
     nbytes = ws.numel() * ws.element_size()
     _check(lib().attn_decode(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
                              n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+class PagedHostKVCache:
+    """A pool of 16-token pages in pinned, mapped host memory (hipHostMalloc), read and written
+    in place by the kernels, with a free list of physical pages. `k` and `v` are numpy views
+    [n_pages, n_kv_heads, 16, head_dim] of the pools (uint16 bit patterns for f16/bf16)."""
+
+    def __init__(self, n_pages: int, n_kv_heads: int, head_dim: int, dtype: str):
+        self.desc = dkv_paged_cache()
+        _check(lib().kv_paged_alloc_host(ctypes.byref(self.desc), n_pages, n_kv_heads, head_dim, DTYPE_CODES[dtype]))
+        self.dtype = dtype
+        self.shape = (n_pages, n_kv_heads, PAGE_TOKENS, head_dim)
+        ctype = ctypes.c_float if dtype == "f32" else ctypes.c_uint16
+        n = n_pages * n_kv_heads * PAGE_TOKENS * head_dim
+        self.k = np.ctypeslib.as_array(ctypes.cast(self.desc.k, ctypes.POINTER(ctype)), shape=(n,)).reshape(self.shape)
+        self.v = np.ctypeslib.as_array(ctypes.cast(self.desc.v, ctypes.POINTER(ctype)), shape=(n,)).reshape(self.shape)
+        self._free = list(range(n_pages - 1, -1, -1))
+
+    @property
+    def n_pages(self):
+        return self.shape[0]
+
+    @property
+    def n_kv_heads(self):
+        return self.shape[1]
+
+    @property
+    def head_dim(self):
+        return self.shape[3]
+
+    def page_bytes(self) -> int:
+        """Bytes of one page, K and V."""
+        return 2 * self.k[0].nbytes
+
+    def allocate(self, n: int) -> list:
+        """Take n free physical pages (raises if the pool is short)."""
+        if n > len(self._free):
+            raise MemoryError(f"{n} pages requested, {len(self._free)} free")
+        return [self._free.pop() for _ in range(n)]
+
+    def release(self, pages) -> None:
+        self._free.extend(int(p) for p in pages)
+
+    def memory_stats(self) -> dict:
+        """Host bytes of the pool (total and in use); the cache holds no device memory."""
+        used = self.n_pages - len(self._free)
+        return {"host_bytes_total": self.n_pages * self.page_bytes(), "host_bytes_used": used * self.page_bytes(),
+                "device_bytes": 0, "pages_used": used, "pages_free": len(self._free)}
+
+    def free(self) -> None:
+        if self.desc.reserved:
+            self.k = self.v = None
+            lib().kv_paged_free_host(ctypes.byref(self.desc))
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def block_table(page_lists, max_pages: int) -> np.ndarray:
+    """int32 [batch, max_pages] block table from per-sequence lists of physical pages (unused
+    entries -1)."""
+    t = np.full((len(page_lists), max_pages), -1, dtype=np.int32)
+    for b, pages in enumerate(page_lists):
+        if len(pages) > max_pages:
+            raise ValueError(f"sequence {b} maps {len(pages)} pages > max_pages={max_pages}")
+        t[b, :len(pages)] = pages
+    return t
+
+
+def _table(table, batch: int):
+    t = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+    if t.ndim != 2 or t.shape[0] != batch:
+        raise ValueError(f"block table must have shape ({batch}, max_pages), got {t.shape}")
+    return t, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), t.shape[1]
+
+
+def paged_workspace_bytes(phase: str, cache: PagedHostKVCache, batch: int, T: int, n_q_heads: int,
+                          max_pages: int) -> int:
+    ph = {"prefill": 0, "decode": 1, "append": 2}[phase]
+    return int(lib().attn_paged_workspace_bytes(ph, ctypes.byref(cache.desc), batch, T, n_q_heads, max_pages))
+
+
+def kv_paged_append(cache: PagedHostKVCache, table, x, wk, wv, past_len, ws, stream=None) -> None:
+    """kv_append into the pages the block table names. x: [B, T, D]."""
+    B, T, D = x.shape
+    lens, lp = _lens(past_len, B)
+    t, tp, mp = _table(table, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().kv_paged_append(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wk), _ptr(wv), lp, B, T, D,
+                                 _ptr(ws), nbytes, _stream(stream)))
+
+
+def attn_prefill_paged(cache: PagedHostKVCache, table, x, wq, wk, wv, past_len, n_q_heads: int, out, ws,
+                       stream=None) -> None:
+    """attn_prefill on a paged cache; out: [B, T, Hq*d] device tensor."""
+    B, T, D = x.shape
+    lens, lp = _lens(past_len, B)
+    t, tp, mp = _table(table, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().attn_prefill_paged(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
+                                    B, T, D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def attn_decode_paged(cache: PagedHostKVCache, table, x, wq, wk, wv, past_len, n_q_heads: int, out, ws,
+                      stream=None) -> None:
+    """attn_decode on a paged cache; x: [B, 1, D] (or [B, D]); out: [B, 1, Hq*d]."""
+    B, D = x.shape[0], x.shape[-1]
+    lens, lp = _lens(past_len, B)
+    t, tp, mp = _table(table, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().attn_decode_paged(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
+                                   B, D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
 def hostlink_stream(host_ptr: int, nbytes: int, mode: str, n_wg: int = 1024, stream=None) -> None:

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/directkv.h"
 #include "dkv_internal.h"
@@ -113,7 +114,7 @@ int decode_target_splits(const dkv_cache* c) {
   return std::max(1, kDecodeWgPerCu * 256 / c->n_kv_heads);
 }
 
-void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, DecodePlan& p) {
+void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, bool paged, DecodePlan& p) {
   int64_t keys = 0;
   for (int b = 0; b < batch; ++b) keys += past_len[b] + 1;
   const int target = decode_target_splits(c);
@@ -121,6 +122,8 @@ void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, Dec
   int64_t chunk = (keys + target - 1) / target;
   chunk = std::max<int64_t>(chunk, 2 * unit);
   chunk = round_up(chunk, unit);
+  // a paged split stages its page ids in LDS: at most kPagedDecodeChunk keys (a multiple of unit)
+  if (paged) chunk = std::min<int64_t>(chunk, kPagedDecodeChunk);
   p.chunk = (int)chunk;
   p.n_splits = 0;
   for (int b = 0; b < batch; ++b) {
@@ -130,9 +133,11 @@ void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, Dec
   p.split_begin[batch] = p.n_splits;
 }
 
-size_t decode_ws_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads) {
-  // sum_b ceil((L_b+1)/chunk) <= keys/chunk + batch <= target + batch
-  const size_t splits = (size_t)decode_target_splits(c) + batch + 1;
+size_t decode_ws_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads, bool paged) {
+  // sum_b ceil((L_b+1)/chunk) <= keys/chunk + batch <= target + batch; a capped paged chunk adds
+  // at most batch * (capacity / kPagedDecodeChunk + 1)
+  size_t splits = (size_t)decode_target_splits(c) + batch + 1;
+  if (paged) splits += (size_t)batch * ((size_t)c->capacity / kPagedDecodeChunk + 1);
   return round_up(splits * n_q_heads * (c->head_dim + 2) * sizeof(float), 256);
 }
 
@@ -154,19 +159,23 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
 }
 
 // keys per super-chunk: the host KV of every (sequence, kv head) pair an XCD serves
-// during one launch must fit about half of that XCD's 4 MB L2
-int superchunk_keys(const dkv_cache* c, int32_t batch) {
+// during one launch must fit about half of that XCD's 4 MB L2 (a quarter for a paged cache:
+// its super-chunk is scattered over the pool in 4 KB (page, head) blocks, which at half the
+// L2 conflict-miss and are fetched again, 1.28x the host bytes against 1.02x at a quarter)
+int superchunk_keys(const dkv_cache* c, int32_t batch, bool paged) {
+  // a paged launch stages the page ids of its keys in LDS: at most kPagedSuperchunk keys
+  const size_t limit = paged ? kPagedSuperchunk : 1 << 20;
   // tuning override (keys, multiple of 64)
   if (const char* env = getenv("DIRECTKV_PREFILL_CHUNK")) {
     const long v = strtol(env, nullptr, 10);
-    if (v >= 64) return (int)(v / 64 * 64);
+    if (v >= 64) return (int)std::min<size_t>(v / 64 * 64, limit);
   }
   const int pairs = batch * c->n_kv_heads;
   const int per_xcd = std::max(1, (pairs + 7) / 8);
   const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);  // K and V
-  size_t keys = ((size_t)2 << 20) / ((size_t)per_xcd * row_bytes);
+  size_t keys = ((size_t)(paged ? 1 : 2) << 20) / ((size_t)per_xcd * row_bytes);
   keys = std::max<size_t>(64, keys / 64 * 64);
-  return (int)std::min<size_t>(keys, 1 << 20);
+  return (int)std::min<size_t>(keys, limit);
 }
 
 // Keys of [k0, k1) visible to the T new tokens of a sequence with past length L (token t
@@ -180,6 +189,12 @@ long long visible_keys(int L, int T, int k0, int k1) {
   const long long c = (long long)L + 1 - k0;   // token t sees c + t keys of the range, unclamped
   return sum_pos(c) - sum_pos(c - (k1 - k0));
 }
+
+// block table of a paged cache, already copied into device memory (null: contiguous cache)
+struct Paging {
+  const int32_t* table = nullptr;
+  int32_t max_pages = 0;
+};
 
 ProjArgs make_proj(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
                    const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
@@ -208,6 +223,273 @@ ProjArgs make_proj(const dkv_cache* c, const void* x, const void* wq, const void
   a.v_dev = v_dev;
   for (int b = 0; b < batch; ++b) a.past_len[b] = past_len[b];
   return a;
+}
+
+}  // namespace
+
+namespace {
+
+// ---- the layer calls, on a contiguous cache or (with a device block table) on a page pool
+// described by a dkv_cache view; arguments are checked by the caller through check_call
+
+int run_append(const dkv_cache* c, const Paging& pg, const void* x, const void* wk, const void* wv,
+               const int32_t* past_len, int32_t batch, int32_t T, int32_t D, hipStream_t s) {
+  proj_fn f = find_proj(c->dtype, c->head_dim);
+  if (!f) return fail(DKV_ERR_UNSUPPORTED, "no projection instance for dtype %d head_dim %d", c->dtype, c->head_dim);
+  ProjArgs a = make_proj(c, x, nullptr, wk, wv, past_len, batch, T, D, 0, nullptr, nullptr, nullptr);
+  a.host_out = 1;
+  a.table = pg.table;
+  a.max_pages = pg.max_pages;
+  hipError_t e = f(a, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return DKV_OK;
+}
+
+int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* wq, const void* wk,
+               const void* wv, const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out,
+               void* ws, size_t ws_bytes, hipStream_t s) {
+  const bool paged = pg.table != nullptr;
+  const size_t need = decode_ws_bytes(c, batch, n_q_heads, paged);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  const int G = n_q_heads / c->n_kv_heads;
+  decode_fn fd = find_decode(c->dtype, c->head_dim, G, paged);
+  combine_fn fc = find_combine(c->dtype, c->head_dim);
+  if (!fd || !fc) return fail(DKV_ERR_UNSUPPORTED, "no decode instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+
+  DecodePlan p;
+  plan_decode(c, past_len, batch, paged, p);
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.wq = wq;
+  a.wk = wk;
+  a.wv = wv;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.part = reinterpret_cast<float*>(ws);
+  a.B = batch;
+  a.D = D;
+  a.Hq = n_q_heads;
+  a.Hkv = c->n_kv_heads;
+  a.cap = c->capacity;
+  a.n_splits = p.n_splits;
+  a.chunk = p.chunk;
+  a.table = pg.table;
+  a.max_pages = pg.max_pages;
+  for (int b = 0; b < batch; ++b) a.past_len[b] = past_len[b];
+  for (int b = 0; b <= batch; ++b) a.split_begin[b] = p.split_begin[b];
+
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.part = a.part;
+  ca.out = out;
+  ca.B = batch;
+  ca.Hq = n_q_heads;
+  ca.n_splits = p.n_splits;
+  for (int b = 0; b <= batch; ++b) ca.split_begin[b] = p.split_begin[b];
+
+  hipError_t e = fd(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = fc(ca, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return DKV_OK;
+}
+
+int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void* wq, const void* wk,
+                const void* wv, const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
+                void* out, void* ws, size_t ws_bytes, hipStream_t s, int32_t variant) {
+  const bool paged = pg.table != nullptr;
+  const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads);
+  if (!ws || ws_bytes < lay.total || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, lay.total);
+  const int G = n_q_heads / c->n_kv_heads;
+  proj_fn fp = find_proj(c->dtype, c->head_dim);
+  attn_fn fa = find_attn(c->dtype, c->head_dim, G, paged);
+  if (!fp || !fa) return fail(DKV_ERR_UNSUPPORTED, "no prefill instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+
+  char* w = reinterpret_cast<char*>(ws);
+  void* q = w + lay.q;
+  void* kn = w + lay.k_new;
+  void* vn = w + lay.v_new;
+  float* state = reinterpret_cast<float*>(w + lay.state);
+
+  const bool separate = variant == DKV_PREFILL_SEPARATE;
+  ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
+                          separate ? nullptr : vn);
+  // the fused path leaves the new rows in device memory here and writes the host copy from
+  // attention launches (below); the baselines write them from the GEMM
+  pa.host_out = variant != DKV_PREFILL_FUSED;
+  pa.table = pg.table;
+  pa.max_pages = pg.max_pages;
+  hipError_t e = fp(pa, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+
+  AttnArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.q = q;
+  aa.kc = c->k;
+  aa.vc = c->v;
+  aa.k_new = kn;
+  aa.v_new = vn;
+  aa.state = state;
+  aa.out = out;
+  aa.B = batch;
+  aa.T = T;
+  aa.Hq = n_q_heads;
+  aa.Hkv = c->n_kv_heads;
+  aa.cap = c->capacity;
+  aa.table = pg.table;
+  aa.max_pages = pg.max_pages;
+  const int rows = attn_rows_per_tile();
+  aa.q_tiles = (T * G + rows - 1) / rows;
+  aa.xcd_group = variant != DKV_PREFILL_NAIVE && batch * c->n_kv_heads >= 8;
+  aa.new_from_host = separate;
+  int max_keys = 0;
+  for (int b = 0; b < batch; ++b) {
+    aa.past_len[b] = past_len[b];
+    max_keys = std::max(max_keys, past_len[b] + T);
+  }
+  // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
+  const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, batch, paged);
+  const int nsc = (max_keys + sk - 1) / sk;
+  // The new rows' host copies are written by launches whose keys hold no host rows (no
+  // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
+  // super-chunk from L2; with no such launch, the last one writes them all. The rows are
+  // split among those launches in proportion to their attention work.
+  int max_past = 0;
+  for (int b = 0; b < batch; ++b) max_past = std::max(max_past, past_len[b]);
+  int first_free = nsc - 1;
+  for (int i = 0; i < nsc; ++i)
+    if (i * sk >= max_past) { first_free = i; break; }
+  auto launch_work = [&](int i) {
+    long long wk_ = 0;
+    for (int b = 0; b < batch; ++b) wk_ += visible_keys(past_len[b], T, i * sk, std::min((i + 1) * sk, max_keys));
+    return wk_;
+  };
+  long long work_total = 0;
+  for (int i = first_free; i < nsc; ++i) work_total += launch_work(i);
+  const long long new_rows = (long long)batch * c->n_kv_heads * T;
+  long long work_before = 0;
+  for (int i = 0; i < nsc; ++i) {
+    aa.kc0 = i * sk;
+    aa.kc1 = std::min((i + 1) * sk, max_keys);
+    aa.first = i == 0;
+    aa.last = i == nsc - 1;
+    aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
+    if (aa.store_new) {
+      const long long wl = launch_work(i);
+      if (work_total > 0) {
+        aa.store_lo = (int)(new_rows * work_before / work_total);
+        aa.store_hi = (int)(new_rows * (work_before + wl) / work_total);
+      } else {
+        aa.store_lo = (int)(new_rows * (i - first_free) / (nsc - first_free));
+        aa.store_hi = (int)(new_rows * (i - first_free + 1) / (nsc - first_free));
+      }
+      work_before += wl;
+    }
+    e = fa(aa, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  return DKV_OK;
+}
+
+// ---- paged caches
+constexpr int32_t kPagedMagic = 0x444B5650;  // marks descriptors made by kv_paged_alloc_host
+
+int check_paged(const dkv_paged_cache* pc) {
+  if (!pc) return fail(DKV_ERR_INVALID_ARG, "paged cache descriptor is null");
+  if (pc->reserved != kPagedMagic || !pc->k || !pc->v)
+    return fail(DKV_ERR_INVALID_ARG, "paged cache descriptor was not made by kv_paged_alloc_host (or was freed)");
+  if (pc->dtype < DKV_F32 || pc->dtype > DKV_BF16) return fail(DKV_ERR_UNSUPPORTED, "dtype %d", pc->dtype);
+  if (pc->head_dim != 64 && pc->head_dim != 128)
+    return fail(DKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", pc->head_dim);
+  if (pc->n_pages <= 0 || pc->n_kv_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "paged cache sizes must be positive");
+  return DKV_OK;
+}
+
+// a dkv_cache view of a page pool for one call: capacity is what the table can address
+dkv_cache paged_view(const dkv_paged_cache* pc, int32_t batch, int32_t max_pages) {
+  dkv_cache c;
+  memset(&c, 0, sizeof(c));
+  c.k = pc->k;
+  c.v = pc->v;
+  c.batch = batch;
+  c.n_kv_heads = pc->n_kv_heads;
+  c.head_dim = pc->head_dim;
+  c.capacity = (int32_t)std::min<int64_t>((int64_t)max_pages * kPageTokens, INT32_MAX / 2);
+  c.dtype = pc->dtype;
+  c.reserved = kMagic;
+  return c;
+}
+
+size_t table_bytes(int32_t batch, int32_t max_pages) { return round_up((size_t)batch * max_pages * 4, 256); }
+
+// Checks the block table on the host before any kernel can follow it: every page that holds
+// a row of [0, past_len[b] + T) is in [0, n_pages), and every page this call writes (rows
+// [past_len[b], past_len[b] + T)) is mapped exactly once in the used part of the table.
+int check_table(const dkv_paged_cache* pc, const int32_t* table, int32_t max_pages, const int32_t* past_len,
+                int32_t batch, int32_t T) {
+  if (!table) return fail(DKV_ERR_INVALID_ARG, "block_table is null");
+  if (max_pages <= 0) return fail(DKV_ERR_INVALID_ARG, "max_pages must be positive");
+  if (batch <= 0) return fail(DKV_ERR_INVALID_ARG, "batch must be positive");
+  if (batch > kMaxBatch) return fail(DKV_ERR_UNSUPPORTED, "batch %d > %d", batch, kMaxBatch);
+  if (!past_len) return fail(DKV_ERR_INVALID_ARG, "past_len is null");
+  if (T < 0) return fail(DKV_ERR_INVALID_ARG, "T must be >= 0");
+  for (int b = 0; b < batch; ++b) {
+    if (past_len[b] < 0) return fail(DKV_ERR_CAPACITY, "past_len[%d]=%d < 0", b, past_len[b]);
+    if ((int64_t)past_len[b] + T > (int64_t)max_pages * kPageTokens)
+      return fail(DKV_ERR_CAPACITY, "past_len[%d]=%d + T=%d exceeds max_pages*%d", b, past_len[b], T, kPageTokens);
+  }
+  thread_local std::vector<int32_t> refs;
+  refs.assign((size_t)pc->n_pages, 0);
+  for (int b = 0; b < batch; ++b) {
+    const int used = (past_len[b] + T + kPageTokens - 1) / kPageTokens;
+    for (int p = 0; p < used; ++p) {
+      const int32_t id = table[(size_t)b * max_pages + p];
+      if (id < 0 || id >= pc->n_pages)
+        return fail(DKV_ERR_INVALID_ARG, "block_table[%d][%d]=%d is outside [0, %d)", b, p, id, pc->n_pages);
+      ++refs[(size_t)id];
+    }
+  }
+  if (T > 0) {
+    for (int b = 0; b < batch; ++b) {
+      for (int p = past_len[b] / kPageTokens; p <= (past_len[b] + T - 1) / kPageTokens; ++p) {
+        const int32_t id = table[(size_t)b * max_pages + p];
+        if (refs[(size_t)id] != 1)
+          return fail(DKV_ERR_INVALID_ARG, "page %d written by sequence %d (block_table[%d][%d]) is mapped %d times",
+                      id, b, b, p, refs[(size_t)id]);
+      }
+    }
+  }
+  return DKV_OK;
+}
+
+// copies the checked table to the front of the workspace; returns the device table
+Paging stage_table(const int32_t* table, int32_t batch, int32_t max_pages, void* ws, hipStream_t s, hipError_t& e) {
+  Paging pg;
+  pg.table = reinterpret_cast<const int32_t*>(ws);
+  pg.max_pages = max_pages;
+  e = hipMemcpyAsync(ws, table, (size_t)batch * max_pages * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  return pg;
+}
+
+// common front of the paged calls: descriptor, table, workspace; on success `view` and `pg`
+// describe the call and the workspace past the table is returned in ws_rest/ws_rest_bytes
+int paged_front(const dkv_paged_cache* pc, const int32_t* table, int32_t max_pages, const int32_t* past_len,
+                int32_t batch, int32_t T, void* ws, size_t ws_bytes, size_t need_rest, hipStream_t s,
+                dkv_cache& view, Paging& pg, void*& ws_rest, size_t& ws_rest_bytes) {
+  int st = check_paged(pc);
+  if (st) return st;
+  if ((st = check_table(pc, table, max_pages, past_len, batch, T))) return st;
+  const size_t tb = table_bytes(batch, max_pages);
+  if (!ws || ws_bytes < tb + need_rest || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, tb + need_rest);
+  view = paged_view(pc, batch, max_pages);
+  ws_rest = reinterpret_cast<char*>(ws) + tb;
+  ws_rest_bytes = ws_bytes - tb;
+  (void)s;
+  return DKV_OK;
 }
 
 }  // namespace
@@ -269,20 +551,14 @@ int kv_append(const dkv_cache* c, const void* x, const void* wk, const void* wv,
   int st = check_call(c, batch, T, D, past_len, {x, wk, wv});
   if (st) return st;
   if (T == 0) return DKV_OK;
-  proj_fn f = find_proj(c->dtype, c->head_dim);
-  if (!f) return fail(DKV_ERR_UNSUPPORTED, "no projection instance for dtype %d head_dim %d", c->dtype, c->head_dim);
-  ProjArgs a = make_proj(c, x, nullptr, wk, wv, past_len, batch, T, D, 0, nullptr, nullptr, nullptr);
-  a.host_out = 1;
-  hipError_t e = f(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
-  return DKV_OK;
+  return run_append(c, Paging{}, x, wk, wv, past_len, batch, T, D, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t attn_workspace_bytes(int32_t phase, const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads,
                             const int32_t* past_len) {
   (void)past_len;
   if (check_cache(c) || batch <= 0 || n_q_heads <= 0 || T < 0) return 0;
-  if (phase == 1) return decode_ws_bytes(c, batch, n_q_heads);
+  if (phase == 1) return decode_ws_bytes(c, batch, n_q_heads, false);
   if (phase == 0) return prefill_layout(c, batch, T, n_q_heads).total;
   return 0;
 }
@@ -294,50 +570,8 @@ int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* w
   if (st) return st;
   if ((st = check_heads(c, n_q_heads))) return st;
   if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
-  const size_t need = decode_ws_bytes(c, batch, n_q_heads);
-  if (!ws || ws_bytes < need || !aligned16(ws))
-    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
-  const int G = n_q_heads / c->n_kv_heads;
-  decode_fn fd = find_decode(c->dtype, c->head_dim, G);
-  combine_fn fc = find_combine(c->dtype, c->head_dim);
-  if (!fd || !fc) return fail(DKV_ERR_UNSUPPORTED, "no decode instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
-
-  DecodePlan p;
-  plan_decode(c, past_len, batch, p);
-  DecodeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.x = x;
-  a.wq = wq;
-  a.wk = wk;
-  a.wv = wv;
-  a.kc = c->k;
-  a.vc = c->v;
-  a.part = reinterpret_cast<float*>(ws);
-  a.B = batch;
-  a.D = D;
-  a.Hq = n_q_heads;
-  a.Hkv = c->n_kv_heads;
-  a.cap = c->capacity;
-  a.n_splits = p.n_splits;
-  a.chunk = p.chunk;
-  for (int b = 0; b < batch; ++b) a.past_len[b] = past_len[b];
-  for (int b = 0; b <= batch; ++b) a.split_begin[b] = p.split_begin[b];
-
-  CombineArgs ca;
-  memset(&ca, 0, sizeof(ca));
-  ca.part = a.part;
-  ca.out = out;
-  ca.B = batch;
-  ca.Hq = n_q_heads;
-  ca.n_splits = p.n_splits;
-  for (int b = 0; b <= batch; ++b) ca.split_begin[b] = p.split_begin[b];
-
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = fd(a, s);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  e = fc(ca, s);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
-  return DKV_OK;
+  return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
@@ -356,95 +590,133 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_SEPARATE)
     return fail(DKV_ERR_INVALID_ARG, "unknown prefill variant %d", variant);
   if (T == 0) return DKV_OK;
-  const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads);
-  if (!ws || ws_bytes < lay.total || !aligned16(ws))
-    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, lay.total);
-  const int G = n_q_heads / c->n_kv_heads;
-  proj_fn fp = find_proj(c->dtype, c->head_dim);
-  attn_fn fa = find_attn(c->dtype, c->head_dim, G);
-  if (!fp || !fa) return fail(DKV_ERR_UNSUPPORTED, "no prefill instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+  return run_prefill(c, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream), variant);
+}
 
-  char* w = reinterpret_cast<char*>(ws);
-  void* q = w + lay.q;
-  void* kn = w + lay.k_new;
-  void* vn = w + lay.v_new;
-  float* state = reinterpret_cast<float*>(w + lay.state);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
-  const bool separate = variant == DKV_PREFILL_SEPARATE;
-  ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
-                          separate ? nullptr : vn);
-  // the fused path leaves the new rows in device memory here and writes the host copy from
-  // attention launches (see below and attn.hip); the baselines write them from the GEMM
-  pa.host_out = variant != DKV_PREFILL_FUSED;
-  hipError_t e = fp(pa, s);
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
-
-  AttnArgs aa;
-  memset(&aa, 0, sizeof(aa));
-  aa.q = q;
-  aa.kc = c->k;
-  aa.vc = c->v;
-  aa.k_new = kn;
-  aa.v_new = vn;
-  aa.state = state;
-  aa.out = out;
-  aa.B = batch;
-  aa.T = T;
-  aa.Hq = n_q_heads;
-  aa.Hkv = c->n_kv_heads;
-  aa.cap = c->capacity;
-  const int rows = attn_rows_per_tile();
-  aa.q_tiles = (T * G + rows - 1) / rows;
-  aa.xcd_group = variant != DKV_PREFILL_NAIVE && batch * c->n_kv_heads >= 8;
-  aa.new_from_host = separate;
-  int max_keys = 0;
-  for (int b = 0; b < batch; ++b) {
-    aa.past_len[b] = past_len[b];
-    max_keys = std::max(max_keys, past_len[b] + T);
+int kv_paged_alloc_host(dkv_paged_cache* out, int32_t n_pages, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t dtype) {
+  if (!out) return fail(DKV_ERR_INVALID_ARG, "out is null");
+  memset(out, 0, sizeof(*out));
+  if (n_pages <= 0 || n_kv_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "n_pages and n_kv_heads must be positive");
+  if (dtype < DKV_F32 || dtype > DKV_BF16) return fail(DKV_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  const size_t bytes = (size_t)n_pages * n_kv_heads * kPageTokens * head_dim * elem_size(dtype);
+  void *k = nullptr, *v = nullptr;
+  const unsigned flags = hipHostMallocMapped | hipHostMallocCoherent;
+  hipError_t e = hipHostMalloc(&k, bytes, flags);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DKV_ERR_HOST_ALLOC, "hipHostMalloc(%zu bytes) for the K pages: %s", bytes, hipGetErrorString(e));
   }
-  // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
-  const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, batch);
-  const int nsc = (max_keys + sk - 1) / sk;
-  // The new rows' host copies are written by launches whose keys hold no host rows (no
-  // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
-  // super-chunk from L2; with no such launch, the last one writes them all. The rows are
-  // split among those launches in proportion to their attention work.
-  int max_past = 0;
-  for (int b = 0; b < batch; ++b) max_past = std::max(max_past, past_len[b]);
-  int first_free = nsc - 1;
-  for (int i = 0; i < nsc; ++i)
-    if (i * sk >= max_past) { first_free = i; break; }
-  auto launch_work = [&](int i) {
-    long long w = 0;
-    for (int b = 0; b < batch; ++b) w += visible_keys(past_len[b], T, i * sk, std::min((i + 1) * sk, max_keys));
-    return w;
-  };
-  long long work_total = 0;
-  for (int i = first_free; i < nsc; ++i) work_total += launch_work(i);
-  const long long new_rows = (long long)batch * c->n_kv_heads * T;
-  long long work_before = 0;
-  for (int i = 0; i < nsc; ++i) {
-    aa.kc0 = i * sk;
-    aa.kc1 = std::min((i + 1) * sk, max_keys);
-    aa.first = i == 0;
-    aa.last = i == nsc - 1;
-    aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
-    if (aa.store_new) {
-      const long long w = launch_work(i);
-      if (work_total > 0) {
-        aa.store_lo = (int)(new_rows * work_before / work_total);
-        aa.store_hi = (int)(new_rows * (work_before + w) / work_total);
-      } else {
-        aa.store_lo = (int)(new_rows * (i - first_free) / (nsc - first_free));
-        aa.store_hi = (int)(new_rows * (i - first_free + 1) / (nsc - first_free));
-      }
-      work_before += w;
-    }
-    e = fa(aa, s);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  e = hipHostMalloc(&v, bytes, flags);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipHostFree(k);
+    return fail(DKV_ERR_HOST_ALLOC, "hipHostMalloc(%zu bytes) for the V pages: %s", bytes, hipGetErrorString(e));
   }
+  out->k = k;
+  out->v = v;
+  out->n_pages = n_pages;
+  out->n_kv_heads = n_kv_heads;
+  out->head_dim = head_dim;
+  out->dtype = dtype;
+  out->reserved = kPagedMagic;
   return DKV_OK;
+}
+
+int kv_paged_free_host(dkv_paged_cache* c) {
+  if (!c) return DKV_OK;
+  if (c->reserved == kPagedMagic) {
+    if (c->k) (void)hipHostFree(c->k);
+    if (c->v) (void)hipHostFree(c->v);
+  }
+  memset(c, 0, sizeof(*c));
+  return DKV_OK;
+}
+
+size_t attn_paged_workspace_bytes(int32_t phase, const dkv_paged_cache* c, int32_t batch, int32_t T,
+                                  int32_t n_q_heads, int32_t max_pages) {
+  if (check_paged(c) || batch <= 0 || batch > kMaxBatch || T < 0 || max_pages <= 0) return 0;
+  const dkv_cache view = paged_view(c, batch, max_pages);
+  const size_t tb = table_bytes(batch, max_pages);
+  if (phase == 2) return tb;
+  if (n_q_heads <= 0) return 0;
+  if (phase == 1) return tb + decode_ws_bytes(&view, batch, n_q_heads, true);
+  if (phase == 0) return tb + prefill_layout(&view, batch, T, n_q_heads).total;
+  return 0;
+}
+
+int kv_paged_append(const dkv_paged_cache* c, const int32_t* block_table, int32_t max_pages, const void* x,
+                    const void* wk, const void* wv, const int32_t* past_len, int32_t batch, int32_t T, int32_t D,
+                    void* ws, size_t ws_bytes, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dkv_cache view;
+  Paging pg;
+  void* rest;
+  size_t rest_bytes;
+  int st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, 0, s, view, pg, rest, rest_bytes);
+  if (st) return st;
+  if ((st = check_call(&view, batch, T, D, past_len, {x, wk, wv}))) return st;
+  if (T == 0) return DKV_OK;
+  hipError_t e;
+  pg = stage_table(block_table, batch, max_pages, ws, s, e);
+  if (e != hipSuccess) return hip_fail(e, "block table copy");
+  return run_append(&view, pg, x, wk, wv, past_len, batch, T, D, s);
+}
+
+int attn_decode_paged(const dkv_paged_cache* c, const int32_t* block_table, int32_t max_pages, const void* x,
+                      const void* wq, const void* wk, const void* wv, const int32_t* past_len, int32_t batch,
+                      int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dkv_cache view;
+  Paging pg;
+  void* rest;
+  size_t rest_bytes;
+  int st = check_paged(c);
+  if (st) return st;
+  if (batch <= 0 || batch > kMaxBatch || max_pages <= 0)
+    return fail(DKV_ERR_INVALID_ARG, "batch must be in [1, %d] and max_pages positive", kMaxBatch);
+  const dkv_cache pre = paged_view(c, batch, max_pages);
+  if (n_q_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "n_q_heads must be positive");
+  const size_t need = decode_ws_bytes(&pre, batch, n_q_heads, true);
+  st = paged_front(c, block_table, max_pages, past_len, batch, 1, ws, ws_bytes, need, s, view, pg, rest, rest_bytes);
+  if (st) return st;
+  if ((st = check_call(&view, batch, 1, D, past_len, {x, wq, wk, wv, out}))) return st;
+  if ((st = check_heads(&view, n_q_heads))) return st;
+  if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
+  hipError_t e;
+  pg = stage_table(block_table, batch, max_pages, ws, s, e);
+  if (e != hipSuccess) return hip_fail(e, "block table copy");
+  return run_decode(&view, pg, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, rest, rest_bytes, s);
+}
+
+int attn_prefill_paged(const dkv_paged_cache* c, const int32_t* block_table, int32_t max_pages, const void* x,
+                       const void* wq, const void* wk, const void* wv, const int32_t* past_len, int32_t batch,
+                       int32_t T, int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dkv_cache view;
+  Paging pg;
+  void* rest;
+  size_t rest_bytes;
+  int st = check_paged(c);
+  if (st) return st;
+  if (batch <= 0 || batch > kMaxBatch || max_pages <= 0 || T < 0)
+    return fail(DKV_ERR_INVALID_ARG, "batch must be in [1, %d], max_pages positive and T >= 0", kMaxBatch);
+  if (n_q_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "n_q_heads must be positive");
+  const dkv_cache pre = paged_view(c, batch, max_pages);
+  const size_t need = prefill_layout(&pre, batch, T, n_q_heads).total;
+  st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, need, s, view, pg, rest, rest_bytes);
+  if (st) return st;
+  if ((st = check_call(&view, batch, T, D, past_len, {x, wq, wk, wv, out}))) return st;
+  if ((st = check_heads(&view, n_q_heads))) return st;
+  if (T == 0) return DKV_OK;
+  hipError_t e;
+  pg = stage_table(block_table, batch, max_pages, ws, s, e);
+  if (e != hipSuccess) return hip_fail(e, "block table copy");
+  return run_prefill(&view, pg, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, rest, rest_bytes, s,
+                     DKV_PREFILL_FUSED);
 }
 
 int dkv_hostlink_stream(void* host_ptr, size_t bytes, int32_t mode, int32_t n_wg, void* stream) {

@@ -61,7 +61,9 @@ struct AttnCfg {
 
 constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max past 2^8
 
-template <typename T, int DH, int G>
+// PAGED: the host cache is a page pool addressed through the block table; the page ids of
+// the launch's host keys are staged in LDS before the sweep.
+template <typename T, int DH, int G, bool PAGED>
 __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
@@ -69,6 +71,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   constexpr int CPR = C::CPR, KPL = MF::KPL, KSTEP = MF::KSTEP;
   __shared__ __attribute__((aligned(16))) T sK[2][C::KTILE];
   __shared__ __attribute__((aligned(16))) T sV[2][C::VTILE];
+  __shared__ int32_t s_pages[PAGED ? kPagedSuperchunk / kPageTokens + 1 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -89,7 +92,8 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       const int pp = row / a.T, t = row - pp * a.T;
       const int bb = pp / a.Hkv;
       const size_t src = ((size_t)pp * a.T + t) * DH + col;
-      const size_t dst = ((size_t)pp * a.cap + a.past_len[bb] + t) * DH + col;
+      const size_t dst = host_row(PAGED ? a.table : nullptr, a.max_pages, bb, pp - bb * a.Hkv, a.Hkv, a.cap,
+                                  a.past_len[bb] + t) * DH + col;
       const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.k_new) + src);
       const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.v_new) + src);
       *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.kc)) + dst) = kv;
@@ -159,12 +163,26 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
     const float sl2 = 1.4426950408889634f * rsqrtf((float)DH);   // log2(e)/sqrt(d)
 
     const size_t bg = (size_t)p;
-    const T* __restrict__ kh = reinterpret_cast<const T*>(a.kc) + bg * a.cap * DH;
-    const T* __restrict__ vh = reinterpret_cast<const T*>(a.vc) + bg * a.cap * DH;
+    const T* __restrict__ kh = reinterpret_cast<const T*>(a.kc) + (PAGED ? 0 : bg * a.cap * DH);
+    const T* __restrict__ vh = reinterpret_cast<const T*>(a.vc) + (PAGED ? 0 : bg * a.cap * DH);
     const T* __restrict__ kn = reinterpret_cast<const T*>(a.k_new) + bg * a.T * DH;
     const T* __restrict__ vn = reinterpret_cast<const T*>(a.v_new) + bg * a.T * DH;
 
     const int host_end = a.new_from_host ? key_hi : L;   // keys below this come from the host
+    const int pg0 = key_lo / kPageTokens;                // first page of the launch's keys
+    if constexpr (PAGED) {
+      const int hend = min(key_hi, host_end);
+      const int npg = hend > key_lo ? (hend - 1) / kPageTokens - pg0 + 1 : 0;
+      for (int i = tid; i < npg; i += C::THREADS) s_pages[i] = a.table[(size_t)b * a.max_pages + pg0 + i];
+      __syncthreads();
+    }
+    // element offset of host key j (row start) within the K or V pool
+    auto hrow = [&](int j) -> size_t {
+      if constexpr (PAGED)
+        return (((size_t)s_pages[j / kPageTokens - pg0] * a.Hkv + g) * kPageTokens + j % kPageTokens) * DH;
+      else
+        return (size_t)j * DH;
+    };
     // this thread's 16-byte chunks of a tile: chunk i is key row krow[i], element offset off[i]
     int krow[LOADS], off[LOADS];
 #pragma unroll
@@ -178,12 +196,21 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       if (j0 + KT <= key_hi && (j0 + KT <= host_end || j0 >= host_end)) {
         // whole tile from one source: one uniform base, per-lane offsets
         const bool host = j0 + KT <= host_end;
-        const T* kb0 = host ? kh + (size_t)j0 * DH : kn + (size_t)(j0 - L) * DH;
-        const T* vb0 = host ? vh + (size_t)j0 * DH : vn + (size_t)(j0 - L) * DH;
+        if (PAGED && host) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          rk[i] = *reinterpret_cast<const uint4*>(kb0 + off[i]);
-          rv[i] = *reinterpret_cast<const uint4*>(vb0 + off[i]);
+          for (int i = 0; i < LOADS; ++i) {
+            const size_t r = hrow(j0 + krow[i]) + (off[i] - krow[i] * DH);
+            rk[i] = *reinterpret_cast<const uint4*>(kh + r);
+            rv[i] = *reinterpret_cast<const uint4*>(vh + r);
+          }
+        } else {
+          const T* kb0 = host ? kh + (size_t)j0 * DH : kn + (size_t)(j0 - L) * DH;
+          const T* vb0 = host ? vh + (size_t)j0 * DH : vn + (size_t)(j0 - L) * DH;
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i) {
+            rk[i] = *reinterpret_cast<const uint4*>(kb0 + off[i]);
+            rv[i] = *reinterpret_cast<const uint4*>(vb0 + off[i]);
+          }
         }
       } else {
 #pragma unroll
@@ -192,8 +219,8 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
           const int e = off[i] - krow[i] * DH;
           if (j < key_hi) {
             const bool host = j < host_end;
-            const T* ks = host ? kh + (size_t)j * DH : kn + (size_t)(j - L) * DH;
-            const T* vs = host ? vh + (size_t)j * DH : vn + (size_t)(j - L) * DH;
+            const T* ks = host ? kh + hrow(j) : kn + (size_t)(j - L) * DH;
+            const T* vs = host ? vh + hrow(j) : vn + (size_t)(j - L) * DH;
             rk[i] = *reinterpret_cast<const uint4*>(ks + e);
             rv[i] = *reinterpret_cast<const uint4*>(vs + e);
           } else {
@@ -349,37 +376,37 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   }
 }
 
-template <typename T, int DH, int G>
+template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int P = a.B * a.Hkv;
   const int grid = a.xcd_group ? 8 * ((P + 7) / 8) * a.q_tiles : P * a.q_tiles;
-  hipLaunchKernelGGL((attn_kernel<T, DH, G>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel<T, DH, G, PAGED>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int DH>
+template <typename T, int DH, bool PAGED>
 static attn_fn pick_g(int G) {
   switch (G) {
-    case 1: return launch_attn<T, DH, 1>;
-    case 2: return launch_attn<T, DH, 2>;
-    case 4: return launch_attn<T, DH, 4>;
-    case 8: return launch_attn<T, DH, 8>;
+    case 1: return launch_attn<T, DH, 1, PAGED>;
+    case 2: return launch_attn<T, DH, 2, PAGED>;
+    case 4: return launch_attn<T, DH, 4, PAGED>;
+    case 8: return launch_attn<T, DH, 8, PAGED>;
     default: return nullptr;
   }
 }
 
 template <typename T>
-static attn_fn pick_d(int d, int G) {
-  if (d == 64) return pick_g<T, 64>(G);
-  if (d == 128) return pick_g<T, 128>(G);
+static attn_fn pick_d(int d, int G, bool paged) {
+  if (d == 64) return paged ? pick_g<T, 64, true>(G) : pick_g<T, 64, false>(G);
+  if (d == 128) return paged ? pick_g<T, 128, true>(G) : pick_g<T, 128, false>(G);
   return nullptr;
 }
 
-attn_fn find_attn(int dtype, int d, int G) {
+attn_fn find_attn(int dtype, int d, int G, bool paged) {
   switch (dtype) {
-    case 0: return pick_d<float>(d, G);
-    case 1: return pick_d<_Float16>(d, G);
-    case 2: return pick_d<__bf16>(d, G);
+    case 0: return pick_d<float>(d, G, paged);
+    case 1: return pick_d<_Float16>(d, G, paged);
+    case 2: return pick_d<__bf16>(d, G, paged);
     default: return nullptr;
   }
 }

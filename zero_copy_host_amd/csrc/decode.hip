@@ -70,13 +70,16 @@ struct DecodeCfg {
   static constexpr int SMEM = MERGE > kMaxD ? MERGE : kMaxD;
 };
 
-template <typename T, int DH, int G>
+// PAGED: the cache is a page pool addressed through the block table; the page ids of this
+// split's rows are staged in LDS first, so row loads never wait on a table load.
+template <typename T, int DH, int G, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   using C = DecodeCfg<T, DH, G>;
   constexpr int VEC = C::VEC, LPR = C::LPR, RPW = C::RPW, NSLOT = C::NSLOT, U = C::U;
   __shared__ float s_buf[C::SMEM];   // activation row, then the per-slot merge area
   __shared__ float s_q[G * DH];
   __shared__ float s_kv[2 * DH];     // the new token's k and v (rounded to T)
+  __shared__ int32_t s_pages[PAGED ? kPagedDecodeChunk / kPageTokens + 1 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.y;
@@ -90,8 +93,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const bool has_new = (k1 == L + 1);
   const int kp_end = min(k1, L);            // host rows [k0, kp_end) are read here
   const size_t bg = (size_t)b * a.Hkv + g;
-  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.kc) + bg * a.cap * DH;
-  const T* __restrict__ vbase = reinterpret_cast<const T*>(a.vc) + bg * a.cap * DH;
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.kc) + (PAGED ? 0 : bg * a.cap * DH);
+  const T* __restrict__ vbase = reinterpret_cast<const T*>(a.vc) + (PAGED ? 0 : bg * a.cap * DH);
+  const int pg0 = k0 / kPageTokens;           // first page of this split
+  if constexpr (PAGED) {
+    const int npg = kp_end > k0 ? (kp_end - 1) / kPageTokens - pg0 + 1 : 0;
+    for (int i = tid; i < npg; i += blockDim.x) s_pages[i] = a.table[(size_t)b * a.max_pages + pg0 + i];
+  }
 
   // ---- projection of this token: q for heads g*G .. g*G+G-1 (and k, v if new)
   const T* __restrict__ xrow = reinterpret_cast<const T*>(a.x) + (size_t)b * a.D;
@@ -108,8 +116,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   if (has_new) {
     // storer: round to the cache dtype and write host row L; attention below uses the
     // rounded values from LDS, never reading the row back over the link
-    T* krow = reinterpret_cast<T*>(a.kc) + (bg * a.cap + L) * DH;
-    T* vrow = reinterpret_cast<T*>(a.vc) + (bg * a.cap + L) * DH;
+    const size_t row = host_row(PAGED ? a.table : nullptr, a.max_pages, b, g, a.Hkv, a.cap, L);
+    T* krow = reinterpret_cast<T*>(a.kc) + row * DH;
+    T* vrow = reinterpret_cast<T*>(a.vc) + row * DH;
     for (int i = tid; i < 2 * DH; i += blockDim.x) {
       const T r = Elem<T>::from_float(s_kv[i]);
       if (i < DH) krow[i] = r; else vrow[i - DH] = r;
@@ -136,8 +145,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
       const int key = base + u * NSLOT + slot;
       if (key < kp_end) {
-        kk[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * DH + col);
-        vv[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * DH + col);
+        size_t row = key;
+        if constexpr (PAGED)
+          row = ((size_t)s_pages[key / kPageTokens - pg0] * a.Hkv + g) * kPageTokens + key % kPageTokens;
+        kk[u] = *reinterpret_cast<const uint4*>(kbase + row * DH + col);
+        vv[u] = *reinterpret_cast<const uint4*>(vbase + row * DH + col);
       } else {
         kk[u] = make_uint4(0, 0, 0, 0);
         vv[u] = make_uint4(0, 0, 0, 0);
@@ -287,9 +299,9 @@ __global__ __launch_bounds__(DH) void combine_kernel(const CombineArgs a) {
   out[i] = Elem<T>::from_float(acc / lsum);
 }
 
-template <typename T, int DH, int G>
+template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<T, DH, G>), dim3(a.n_splits, a.Hkv), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, DH, G, PAGED>), dim3(a.n_splits, a.Hkv), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -299,30 +311,30 @@ static hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---- pre-instantiated kernel table (dtype x head_dim x group size)
-template <typename T, int DH>
+// ---- pre-instantiated kernel table (dtype x head_dim x group size x cache layout)
+template <typename T, int DH, bool PAGED>
 static decode_fn pick_g(int G) {
   switch (G) {
-    case 1: return launch_decode<T, DH, 1>;
-    case 2: return launch_decode<T, DH, 2>;
-    case 4: return launch_decode<T, DH, 4>;
-    case 8: return launch_decode<T, DH, 8>;
+    case 1: return launch_decode<T, DH, 1, PAGED>;
+    case 2: return launch_decode<T, DH, 2, PAGED>;
+    case 4: return launch_decode<T, DH, 4, PAGED>;
+    case 8: return launch_decode<T, DH, 8, PAGED>;
     default: return nullptr;
   }
 }
 
 template <typename T>
-static decode_fn pick_d(int d, int G) {
-  if (d == 64) return pick_g<T, 64>(G);
-  if (d == 128) return pick_g<T, 128>(G);
+static decode_fn pick_d(int d, int G, bool paged) {
+  if (d == 64) return paged ? pick_g<T, 64, true>(G) : pick_g<T, 64, false>(G);
+  if (d == 128) return paged ? pick_g<T, 128, true>(G) : pick_g<T, 128, false>(G);
   return nullptr;
 }
 
-decode_fn find_decode(int dtype, int d, int G) {
+decode_fn find_decode(int dtype, int d, int G, bool paged) {
   switch (dtype) {
-    case 0: return pick_d<float>(d, G);
-    case 1: return pick_d<_Float16>(d, G);
-    case 2: return pick_d<__bf16>(d, G);
+    case 0: return pick_d<float>(d, G, paged);
+    case 1: return pick_d<_Float16>(d, G, paged);
+    case 2: return pick_d<__bf16>(d, G, paged);
     default: return nullptr;
   }
 }

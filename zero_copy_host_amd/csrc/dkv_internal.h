@@ -9,6 +9,9 @@ namespace dkv {
 
 constexpr int kMaxBatch = 256;   // sequences per call (lengths travel in kernel arguments)
 constexpr int kMaxD = 8192;      // model width held in LDS by the decode kernel
+constexpr int kPageTokens = 16;  // token rows per page of a paged host cache
+constexpr int kPagedDecodeChunk = 8192;  // keys per decode split at most, paged caches
+constexpr int kPagedSuperchunk = 16384;  // keys per prefill launch at most, paged caches
 constexpr int kWave = 64;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -99,6 +102,17 @@ template <> struct Mfma<float> {
   }
 };
 
+// Row index (in rows of d elements) of token j of (sequence b, kv head g) in a host cache:
+// contiguous [B][Hkv][cap][d], or paged, pool [n_pages][Hkv][kPageTokens][d] with the page of
+// token j at table[b * max_pages + j / kPageTokens].
+__device__ inline size_t host_row(const int32_t* table, int max_pages, int b, int g, int Hkv, int cap, int j) {
+  if (table) {
+    const int pg = table[(size_t)b * max_pages + j / kPageTokens];
+    return ((size_t)pg * Hkv + g) * kPageTokens + j % kPageTokens;
+  }
+  return ((size_t)b * Hkv + g) * cap + j;
+}
+
 __device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
 // ------------------------------------------------------------------ launch arguments
@@ -115,6 +129,8 @@ struct ProjArgs {
   void* k_dev;              // optional device copy of the new K rows [B, Hkv, T, d]
   void* v_dev;              // optional device copy of the new V rows
   int32_t host_out;         // 1: write the new K/V rows to the host cache (segments 1, 2)
+  const int32_t* table;     // paged cache: device block table [B][max_pages]; null = contiguous
+  int32_t max_pages;
   int32_t past_len[kMaxBatch];
 };
 
@@ -127,6 +143,8 @@ struct DecodeArgs {
   void* vc;
   float* part;              // [n_splits_total][Hq][d + 2]: o (unnormalised), m, l
   int32_t B, D, Hq, Hkv, cap, n_splits;
+  const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
+  int32_t max_pages;
   int32_t past_len[kMaxBatch];
   int32_t split_begin[kMaxBatch + 1];  // first global split of sequence b
   int32_t chunk;                       // keys per split
@@ -157,6 +175,8 @@ struct AttnArgs {
   int32_t new_from_host;    // 1: this step's rows are read back from the host cache too
   int32_t store_new;        // 1: also copy this step's rows from k_new/v_new to the host cache
   int32_t store_lo, store_hi;  // (pair, token) rows [store_lo, store_hi) this launch copies
+  const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
+  int32_t max_pages;
   int32_t past_len[kMaxBatch];
 };
 
@@ -168,9 +188,9 @@ typedef hipError_t (*combine_fn)(const CombineArgs&, hipStream_t);
 typedef hipError_t (*attn_fn)(const AttnArgs&, hipStream_t);
 
 proj_fn find_proj(int dtype, int d);
-decode_fn find_decode(int dtype, int d, int G);
+decode_fn find_decode(int dtype, int d, int G, bool paged);
 combine_fn find_combine(int dtype, int d);
-attn_fn find_attn(int dtype, int d, int G);
+attn_fn find_attn(int dtype, int d, int G, bool paged);
 
 int decode_slots(int dtype, int d);  // key rows one decode WG consumes per step
 int attn_rows_per_tile();            // query rows (token x head) per prefill WG

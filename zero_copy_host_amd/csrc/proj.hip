@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
       const size_t bgk = (size_t)b * a.Hkv + gg;
       if (a.host_out) {
         T* cache = reinterpret_cast<T*>(seg == 1 ? a.kc : a.vc);
-        *reinterpret_cast<uint4*>(cache + (bgk * a.cap + a.past_len[b] + t) * a.d + i) = val;
+        const size_t row = host_row(a.table, a.max_pages, b, gg, a.Hkv, a.cap, a.past_len[b] + t);
+        *reinterpret_cast<uint4*>(cache + row * a.d + i) = val;
       }
       void* dev = seg == 1 ? a.k_dev : a.v_dev;
       if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
