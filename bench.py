@@ -203,7 +203,16 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
            **_prefill_stats(w, past, timed(variant, steps, warmup), peak_read)}
     if ablations:
         # the baselines the pages compare the method against, on the same inputs
-        res["ablations_ms"] = {v: timed(v, 2, 1) for v in ablations}
+        res["ablations_ms"] = {}
+        res["device_workspace_bytes"] = {variant: ws.numel()}
+        for v in ablations:
+            if v == "staged":   # needs a device copy of the whole cache in its workspace
+                del ws
+                torch.cuda.empty_cache()
+                ws = torch.empty(dkv.workspace_bytes("prefill_staged", cache, w.B, w.T, w.Hq), dtype=torch.uint8,
+                                 device="cuda")
+                res["device_workspace_bytes"][v] = ws.numel()
+            res["ablations_ms"][v] = timed(v, 2, 1)
     if decode_steps:
         del out, ws
         xs = [to_dev(dr.normal((w.B, 1, w.D), 1.0, w.dtype), w.dtype) for _ in range(decode_steps)]
@@ -301,6 +310,36 @@ def run_paged(dkv, peak_read=None, decode_steps=10, prefill_steps=3):
     return res
 
 
+def run_staging(dkv, peak_read=None, steps=6):
+    """The 8B decode step read zero-copy (this library) and through the staging baseline (the
+    past rows DMA-copied into a device copy of the cache first, the new rows copied back): time
+    per step and the device memory each call needs."""
+    import torch
+    import synth
+    w = synth.workload("llama8b_decode_b8_L32768_bf16")
+    past, cache, dev, _ = _layer_setup(dkv, w)
+    out = torch.empty((w.B, 1, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
+    res = {"workload": w.name}
+    for var, phase in (("zerocopy", "decode"), ("staged", "decode_staged")):
+        nb = dkv.workspace_bytes(phase, cache, w.B, 1, w.Hq)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            dkv.attn_decode_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
+        torch.cuda.synchronize()
+        with EventTimer() as t:
+            for _ in range(steps):
+                dkv.attn_decode_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
+        ms = t.ms / steps
+        res[var] = {"us_per_step": ms * 1e3, "device_workspace_bytes": nb,
+                    "host_bytes_per_step_GBps": _decode_stats(w, past, ms, peak_read)["host_read_GBps"]}
+        del ws
+        torch.cuda.empty_cache()
+    res["staging_device_bytes"] = res["staged"]["device_workspace_bytes"] - res["zerocopy"]["device_workspace_bytes"]
+    res["host_cache_bytes"] = cache.nbytes()
+    cache.free()
+    return res
+
+
 def bench_prefill(dkv, steps=5, warmup=2):
     return run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps, warmup)
 
@@ -333,9 +372,9 @@ def main():
     ap.add_argument("--variant", default="fused", choices=["fused", "naive", "separate"],
                     help="prefill variant for --profile prefill (the ablation baselines)")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "paged", "calib"],
+    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "paged", "staging", "calib"],
                     help="short run for rocprofv3: decode steps only, prefill steps only, the paged-cache "
-                         "decode and prefill, or the "
+                         "decode and prefill, the staging baseline, or the "
                          "counter calibration kernels (1 GiB host read, 1 GiB host write, 1 GiB "
                          "device-to-device copy)")
     args = ap.parse_args()
@@ -352,6 +391,11 @@ def main():
 
     if args.profile == "calib":
         calibration_kernels(dkv)
+        return
+    if args.profile == "staging":
+        print(json.dumps({"staging_baseline": run_staging(dkv, steps=args.steps),
+                          "prefill": run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=3, warmup=1,
+                                                 ablations=("staged",))}), flush=True)
         return
     if args.profile == "paged":
         print(json.dumps({"paged": run_paged(dkv, decode_steps=args.steps, prefill_steps=max(1, args.steps // 3))}),
@@ -429,7 +473,9 @@ def main():
         tiny = run_prefill(dkv, "tiny_f32_prefill128_decode1", steps=20, warmup=3, peak_read=pr, decode_steps=1)
         log("8B chunked prefill")
         result["prefill"] = run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=5, warmup=2, peak_read=pr,
-                                        ablations=("naive", "separate"))
+                                        ablations=("naive", "separate", "staged"))
+        log("staging baseline: 8B decode")
+        result["staging_baseline"] = run_staging(dkv, peak_read=pr)
         log("long-context fp16 decode")
         longd = run_decode(dkv, "long_decode_b4_L96k_128k_f16", steps=6, warmup=1, peak_read=pr)
         log("70B prefill + 64 decode steps")

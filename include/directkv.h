@@ -101,10 +101,11 @@ int kv_append(const dkv_cache* c, const void* x, const void* wk, const void* wv,
 
 /*
  * Device workspace the attention calls need, in bytes (phase 0 = prefill with T new
- * tokens, phase 1 = decode with T = 1). It holds the projected queries, this step's new
- * K/V rows, per-split softmax partials and per-row running softmax state. The caller
- * allocates it (e.g. as a device tensor) and passes it with its size. Returns 0 for an
- * invalid argument.
+ * tokens, phase 1 = decode with T = 1; phases 2 and 3 = the same for the staging baseline,
+ * DKV_PREFILL_STAGED / DKV_DECODE_STAGED, which adds a device copy of the whole cache). It
+ * holds the projected queries, this step's new K/V rows, per-split softmax partials and
+ * per-row running softmax state. The caller allocates it (e.g. as a device tensor) and
+ * passes it with its size. Returns 0 for an invalid argument.
  */
 size_t attn_workspace_bytes(int32_t phase, const dkv_cache* c, int32_t batch, int32_t T,
                             int32_t n_q_heads, const int32_t* past_len);
@@ -124,17 +125,22 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
 
 /*
  * Ablation baselines for the comparisons the pages report ([N] Experiments & Results:
- * CPU-aware tiling vs naive zero-copy, Fig. 12; fused vs separate kernels, Fig. 13). Same
- * arguments, results and errors as attn_prefill; `variant` selects how the host cache is read:
+ * CPU-aware tiling vs naive zero-copy, Fig. 12; fused vs separate kernels, Fig. 13; and the
+ * swap-based offloading that stages KV in GPU memory, [N] Prior work / GPU memory, Fig. 11b).
+ * Same arguments, results and errors as attn_prefill; `variant` selects how the host cache is
+ * read:
  *   DKV_PREFILL_FUSED    the attn_prefill path (host KV fetched once per step, new rows kept
  *                        in device memory);
  *   DKV_PREFILL_NAIVE    query-stationary tiling pointed at host memory: every query tile
  *                        streams the whole cache over the link in one launch;
  *   DKV_PREFILL_SEPARATE projection writes new K/V to the host only, and attention reads
- *                        them back over the link.
+ *                        them back over the link;
+ *   DKV_PREFILL_STAGED   the past rows are first copied (DMA) into a device staging copy of
+ *                        the cache held in the workspace (attn_workspace_bytes phase 2), the
+ *                        fused kernels run on that copy, and the new rows are copied back.
  * Errors: as attn_prefill, plus INVALID_ARG for an unknown variant.
  */
-enum { DKV_PREFILL_FUSED = 0, DKV_PREFILL_NAIVE = 1, DKV_PREFILL_SEPARATE = 2 };
+enum { DKV_PREFILL_FUSED = 0, DKV_PREFILL_NAIVE = 1, DKV_PREFILL_SEPARATE = 2, DKV_PREFILL_STAGED = 3 };
 int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, const void* wk,
                          const void* wv, const int32_t* past_len, int32_t batch, int32_t T,
                          int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes,
@@ -150,6 +156,18 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
 int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* wk,
                 const void* wv, const int32_t* past_len, int32_t batch, int32_t D,
                 int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * attn_decode with the staging baseline selectable: DKV_DECODE_ZEROCOPY is attn_decode;
+ * DKV_DECODE_STAGED first copies rows [0, past_len[b]) of every head into a device copy of
+ * the cache in the workspace (attn_workspace_bytes phase 3), runs the decode kernels on it,
+ * and copies the new rows back to the host cache. Same results as attn_decode.
+ */
+enum { DKV_DECODE_ZEROCOPY = 0, DKV_DECODE_STAGED = 1 };
+int attn_decode_variant(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                        const void* wv, const int32_t* past_len, int32_t batch, int32_t D,
+                        int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream,
+                        int32_t variant);
 
 /*
  * ---- Paged host cache ([N] KV Cache Manager; the page manager of the pages' reference

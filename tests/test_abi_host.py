@@ -94,8 +94,15 @@ def test_call_validation_statuses(dkv):
     bad = _fake_cache(dkv)
     bad.reserved = 0
     assert L.attn_decode(ctypes.byref(bad), x, w, w, w, lp, 2, 256, 4, out, ws, 1 << 30, None) == -1
-    # unknown prefill variant
-    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, 1 << 30, None, 3) == -1
+    # unknown prefill / decode variant
+    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, 1 << 30, None, 4) == -1
+    assert L.attn_decode_variant(ctypes.byref(c), x, w, w, w, lp, 2, 256, 4, out, ws, 1 << 30, None, 2) == -1
+    # the staging baselines check their larger workspace before any copy: what the zero-copy
+    # call needs is too small for them
+    plain_d = L.attn_workspace_bytes(1, ctypes.byref(c), 2, 1, 4, lp)
+    plain_p = L.attn_workspace_bytes(0, ctypes.byref(c), 2, 8, 4, lp)
+    assert L.attn_decode_variant(ctypes.byref(c), x, w, w, w, lp, 2, 256, 4, out, ws, plain_d, None, 1) == -6
+    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, plain_p, None, 3) == -6
     assert L.kv_append(None, x, w, w, lp, 2, 1, 256, None) == -1
     # unsupported head_dim / dtype in a descriptor
     assert L.kv_append(ctypes.byref(_fake_cache(dkv, d=96)), x, w, w, lp, 2, 1, 256, None) == -3
@@ -128,7 +135,11 @@ def test_workspace_sizes(dkv):
     assert want <= ws <= want + 4 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
     assert 0 < wsd < (1 << 24)
-    assert L.attn_workspace_bytes(2, ctypes.byref(c), 1, 1, 32, lp) == 0
+    # staging baselines: a device copy of the whole cache (K and V) on top
+    staging = 2 * 1 * 8 * 32768 * 128 * e
+    assert L.attn_workspace_bytes(2, ctypes.byref(c), 1, 8192, 32, lp) == staging + ws
+    assert L.attn_workspace_bytes(3, ctypes.byref(c), 1, 1, 32, lp) == staging + wsd
+    assert L.attn_workspace_bytes(4, ctypes.byref(c), 1, 1, 32, lp) == 0
     assert L.attn_workspace_bytes(1, None, 1, 1, 32, lp) == 0
 
 

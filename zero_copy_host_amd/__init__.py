@@ -21,11 +21,12 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HOST_ALLOC",
           -5: "HIP", -6: "WORKSPACE"}
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
-           "attn_prefill_variant", "attn_decode", "kv_paged_alloc_host", "kv_paged_free_host",
+           "attn_prefill_variant", "attn_decode", "attn_decode_variant", "kv_paged_alloc_host", "kv_paged_free_host",
            "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
            "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
 PAGE_TOKENS = 16
-PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2}
+PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2, "staged": 3}
+DECODE_VARIANTS = {"zerocopy": 0, "staged": 1}
 
 
 class DirectKVError(RuntimeError):
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_variant.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, I32, VP, VP, SZ,
                                            VP, I32]
         L.attn_decode.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP]
+        L.attn_decode_variant.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP, I32]
         L.kv_paged_alloc_host.argtypes = [P(dkv_paged_cache), I32, I32, I32, I32]
         L.kv_paged_free_host.argtypes = [P(dkv_paged_cache)]
         L.attn_paged_workspace_bytes.argtypes = [I32, P(dkv_paged_cache), I32, I32, I32, I32]
@@ -83,7 +85,7 @@ def lib() -> ctypes.CDLL:
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
         for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
-                     "attn_decode", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
+                     "attn_decode", "attn_decode_variant", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
                      "attn_prefill_paged", "attn_decode_paged", "dkv_hostlink_stream"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -168,7 +170,9 @@ def kv_append(cache: HostKVCache, x, wk, wv, past_len: Sequence[int], stream=Non
 
 
 def workspace_bytes(phase: str, cache: HostKVCache, batch: int, T: int, n_q_heads: int) -> int:
-    ph = {"prefill": 0, "decode": 1}[phase]
+    """Device workspace bytes of a call: "prefill", "decode", or the staging baseline's
+    "prefill_staged" / "decode_staged" (which hold a device copy of the whole cache)."""
+    ph = {"prefill": 0, "decode": 1, "prefill_staged": 2, "decode_staged": 3}[phase]
     return int(lib().attn_workspace_bytes(ph, ctypes.byref(cache.desc), batch, T, n_q_heads, None))
 
 
@@ -314,6 +318,17 @@ def attn_decode_paged(cache: PagedHostKVCache, table, x, wq, wk, wv, past_len, n
     nbytes = ws.numel() * ws.element_size()
     _check(lib().attn_decode_paged(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
                                    B, D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def attn_decode_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, variant: str,
+                        stream=None) -> None:
+    """attn_decode reading the cache as `variant` ("zerocopy", or "staged": DMA into device memory first)."""
+    B, D = x.shape[0], x.shape[-1]
+    lens, lp = _lens(past_len, B)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().attn_decode_variant(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
+                                     n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream),
+                                     DECODE_VARIANTS[variant]))
 
 
 def hostlink_stream(host_ptr: int, nbytes: int, mode: str, n_wg: int = 1024, stream=None) -> None:

@@ -394,6 +394,49 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   return DKV_OK;
 }
 
+// ---- the staging baseline: the past rows are copied into device memory before the kernels
+// run (the swap-based offloading the pages compare against), and the new rows copied back
+
+size_t staging_bytes(const dkv_cache* c) {
+  return round_up((size_t)c->batch * c->n_kv_heads * c->capacity * c->head_dim * elem_size(c->dtype), 256);
+}
+
+// copy token rows [r0[b], r0[b] + n) of every (b, g) between two [B][Hkv][cap][d] caches
+hipError_t copy_rows(void* dst, const void* src, const dkv_cache* c, const int32_t* r0, int32_t n_new,
+                     bool past, hipMemcpyKind kind, hipStream_t s) {
+  const size_t row = (size_t)c->head_dim * elem_size(c->dtype), pitch = (size_t)c->capacity * row;
+  for (int b = 0; b < c->batch; ++b) {
+    const size_t first = past ? 0 : (size_t)r0[b];
+    const size_t n = past ? (size_t)r0[b] : (size_t)n_new;
+    if (n == 0) continue;
+    const size_t off = (size_t)b * c->n_kv_heads * pitch + first * row;
+    hipError_t e = hipMemcpy2DAsync(reinterpret_cast<char*>(dst) + off, pitch,
+                                    reinterpret_cast<const char*>(src) + off, pitch, n * row, c->n_kv_heads, kind, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// a device copy of cache c at the front of the workspace: [K staging][V staging]
+dkv_cache staged_view(const dkv_cache* c, void* ws) {
+  dkv_cache d = *c;
+  d.k = ws;
+  d.v = reinterpret_cast<char*>(ws) + staging_bytes(c);
+  return d;
+}
+
+int stage_in(const dkv_cache* c, const dkv_cache& dev, const int32_t* past_len, hipStream_t s) {
+  hipError_t e = copy_rows(dev.k, c->k, c, past_len, 0, true, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = copy_rows(dev.v, c->v, c, past_len, 0, true, hipMemcpyHostToDevice, s);
+  return e == hipSuccess ? DKV_OK : hip_fail(e, "staging copy to device");
+}
+
+int stage_out(const dkv_cache* c, const dkv_cache& dev, const int32_t* past_len, int32_t T, hipStream_t s) {
+  hipError_t e = copy_rows(c->k, dev.k, c, past_len, T, false, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = copy_rows(c->v, dev.v, c, past_len, T, false, hipMemcpyDeviceToHost, s);
+  return e == hipSuccess ? DKV_OK : hip_fail(e, "new rows back to the host cache");
+}
+
 // ---- paged caches
 constexpr int32_t kPagedMagic = 0x444B5650;  // marks descriptors made by kv_paged_alloc_host
 
@@ -560,18 +603,39 @@ size_t attn_workspace_bytes(int32_t phase, const dkv_cache* c, int32_t batch, in
   if (check_cache(c) || batch <= 0 || n_q_heads <= 0 || T < 0) return 0;
   if (phase == 1) return decode_ws_bytes(c, batch, n_q_heads, false);
   if (phase == 0) return prefill_layout(c, batch, T, n_q_heads).total;
+  if (phase == 2) return 2 * staging_bytes(c) + prefill_layout(c, batch, T, n_q_heads).total;
+  if (phase == 3) return 2 * staging_bytes(c) + decode_ws_bytes(c, batch, n_q_heads, false);
   return 0;
 }
 
 int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
                 const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out, void* ws,
                 size_t ws_bytes, void* stream) {
+  return attn_decode_variant(c, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes, stream,
+                             DKV_DECODE_ZEROCOPY);
+}
+
+int attn_decode_variant(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                        const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out, void* ws,
+                        size_t ws_bytes, void* stream, int32_t variant) {
   int st = check_call(c, batch, 1, D, past_len, {x, wq, wk, wv, out});
   if (st) return st;
   if ((st = check_heads(c, n_q_heads))) return st;
   if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
-  return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes,
-                    reinterpret_cast<hipStream_t>(stream));
+  if (variant != DKV_DECODE_ZEROCOPY && variant != DKV_DECODE_STAGED)
+    return fail(DKV_ERR_INVALID_ARG, "unknown decode variant %d", variant);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (variant == DKV_DECODE_ZEROCOPY)
+    return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes, s);
+  const size_t sb = 2 * staging_bytes(c), need = sb + decode_ws_bytes(c, batch, n_q_heads, false);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  const dkv_cache dev = staged_view(c, ws);
+  if ((st = stage_in(c, dev, past_len, s))) return st;
+  if ((st = run_decode(&dev, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out,
+                       reinterpret_cast<char*>(ws) + sb, ws_bytes - sb, s)))
+    return st;
+  return stage_out(c, dev, past_len, 1, s);
 }
 
 int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
@@ -587,11 +651,21 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   int st = check_call(c, batch, T, D, past_len, {x, wq, wk, wv, out});
   if (st) return st;
   if ((st = check_heads(c, n_q_heads))) return st;
-  if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_SEPARATE)
+  if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_STAGED)
     return fail(DKV_ERR_INVALID_ARG, "unknown prefill variant %d", variant);
   if (T == 0) return DKV_OK;
-  return run_prefill(c, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes,
-                     reinterpret_cast<hipStream_t>(stream), variant);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (variant != DKV_PREFILL_STAGED)
+    return run_prefill(c, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes, s, variant);
+  const size_t sb = 2 * staging_bytes(c), need = sb + prefill_layout(c, batch, T, n_q_heads).total;
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  const dkv_cache dev = staged_view(c, ws);
+  if ((st = stage_in(c, dev, past_len, s))) return st;
+  if ((st = run_prefill(&dev, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out,
+                        reinterpret_cast<char*>(ws) + sb, ws_bytes - sb, s, DKV_PREFILL_FUSED)))
+    return st;
+  return stage_out(c, dev, past_len, T, s);
 }
 
 int kv_paged_alloc_host(dkv_paged_cache* out, int32_t n_pages, int32_t n_kv_heads, int32_t head_dim,
