@@ -340,6 +340,65 @@ def run_staging(dkv, peak_read=None, steps=6):
     return res
 
 
+STACKS = {
+    # name: (layers, batch, past tokens, D, Hq, Hkv, d, F) -- Llama-3-8B- and 70B-shaped decoder stacks
+    "llama8b_32layers_b8_L32768": (32, 8, 32768, 4096, 32, 8, 128, 14336),
+    "llama70b_80layers_b2_L65536": (80, 2, 65536, 8192, 64, 8, 128, 28672),
+}
+
+
+def run_stack(dkv, name, tokens=3, peak_read=None):
+    """Per-token latency of a full decoder stack in the decode phase: every layer has its own
+    host KV cache (past K/V of layer 0 drawn from the workload seed and copied to the other
+    layers; weights drawn on the device from a fixed seed, distinct per layer), and each token
+    runs DecodeStack.step over all layers at advancing lengths."""
+    import torch
+    import synth
+    from zero_copy_host_amd.decode_stack import DecodeStack
+    n_layers, B, L, D, Hq, Hkv, d, F = STACKS[name]
+    dt = "bf16"
+    cap = (L + tokens + 63) // 64 * 64
+    dr = synth.Draw(2000)
+    caches = [dkv.HostKVCache(B, Hkv, d, cap, dt) for _ in range(n_layers)]
+    past = np.full(B, L, dtype=np.int32)
+    synth.fill_past(dr, caches[0].k, caches[0].v, past, dt)
+    for c in caches[1:]:
+        np.copyto(c.k, caches[0].k)
+        np.copyto(c.v, caches[0].v)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2001)
+
+    def w(out_f, in_f):
+        return (torch.randn(out_f, in_f, generator=gen, device="cuda") * in_f ** -0.5).to(torch.bfloat16)
+
+    layers = [{"wq": w(Hq * d, D), "wk": w(Hkv * d, D), "wv": w(Hkv * d, D), "wo": w(D, Hq * d),
+               "w_gu": w(2 * F, D), "w_down": w(D, F),
+               "g_attn": torch.ones(D, dtype=torch.bfloat16, device="cuda"),
+               "g_mlp": torch.ones(D, dtype=torch.bfloat16, device="cuda")} for _ in range(n_layers)]
+    weight_bytes = sum(t.numel() * t.element_size() for lw in layers for t in lw.values())
+    stack = DecodeStack(layers, caches, Hq)
+    h = torch.randn(B, D, generator=gen, device="cuda").to(torch.bfloat16)
+    stack.step(h, past)                   # warm-up token at the first length (rewritten below)
+    torch.cuda.synchronize()
+    with EventTimer() as t:
+        for i in range(tokens):
+            stack.step(h, past + i)
+    ms = t.ms / tokens
+    host_read = n_layers * 2 * B * Hkv * (L + tokens // 2) * d * 2
+    res = {"stack": name, "layers": n_layers, "batch": B, "past_len_first": L, "tokens": tokens,
+           "ms_per_token": ms, "tok_per_s": B / (ms * 1e-3),
+           "host_kv_bytes": sum(c.nbytes() for c in caches), "device_weight_bytes": weight_bytes,
+           "host_read_GBps": host_read / (ms * 1e-3) / 1e9,
+           "attention_share_note": "per layer: attn_decode (host-link bound) + norm/Wo/MLP (HBM)"}
+    if peak_read:
+        res["frac_of_measured_read_peak"] = res["host_read_GBps"] / peak_read
+    del stack, layers, h
+    for c in caches:
+        c.free()
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(dkv, steps=5, warmup=2):
     return run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps, warmup)
 
@@ -372,9 +431,9 @@ def main():
     ap.add_argument("--variant", default="fused", choices=["fused", "naive", "separate"],
                     help="prefill variant for --profile prefill (the ablation baselines)")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "paged", "staging", "calib"],
+    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "paged", "staging", "stack", "calib"],
                     help="short run for rocprofv3: decode steps only, prefill steps only, the paged-cache "
-                         "decode and prefill, the staging baseline, or the "
+                         "decode and prefill, the staging baseline, the 8B/70B decoder stacks, or the "
                          "counter calibration kernels (1 GiB host read, 1 GiB host write, 1 GiB "
                          "device-to-device copy)")
     args = ap.parse_args()
@@ -391,6 +450,13 @@ def main():
 
     if args.profile == "calib":
         calibration_kernels(dkv)
+        return
+    if args.profile == "stack":
+        out = {}
+        for name in STACKS:
+            log(f"decoder stack {name}")
+            out[name] = run_stack(dkv, name, tokens=max(1, args.steps))
+        print(json.dumps({"decode_stack": out}), flush=True)
         return
     if args.profile == "staging":
         print(json.dumps({"staging_baseline": run_staging(dkv, steps=args.steps),
@@ -476,6 +542,9 @@ def main():
                                         ablations=("naive", "separate", "staged"))
         log("staging baseline: 8B decode")
         result["staging_baseline"] = run_staging(dkv, peak_read=pr)
+        log("decoder stack: 32 layers of the 8B layer, per-token latency")
+        result["decode_stack"] = {"llama8b_32layers_b8_L32768": run_stack(dkv, "llama8b_32layers_b8_L32768",
+                                                                          tokens=2, peak_read=pr)}
         log("long-context fp16 decode")
         longd = run_decode(dkv, "long_decode_b4_L96k_128k_f16", steps=6, warmup=1, peak_read=pr)
         log("70B prefill + 64 decode steps")

@@ -233,6 +233,30 @@ int attn_decode_paged(const dkv_paged_cache* c, const int32_t* block_table, int3
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- Decode-loop helpers: the per-layer work around the attention layer in a multi-layer
+ * decode step (a pre-norm decoder block: RMSNorm, the layer, an output projection with a
+ * residual add, RMSNorm, a SwiGLU MLP with a residual add). The pages describe the attention
+ * layer only; these exist so that a stack of layers can run end to end on synthetic weights.
+ * All pointers are caller-owned device memory in the given dtype, rows are row-major.
+ */
+
+/* y[r, :] = x[r, :] / sqrt(mean_i x[r, i]^2 + eps) * weight, for r < rows; fp32 arithmetic,
+ * rounded once to dtype. x, y: [rows, D]; weight: [D]. y may be x itself. */
+int dkv_rmsnorm(const void* x, const void* weight, void* y, int32_t rows, int32_t D, float eps,
+                int32_t dtype, void* stream);
+
+/* y = x·wᵀ (+ residual): x [rows, K], w [N, K] (a linear layer's [out, in] weight), residual
+ * and y [rows, N]; fp32 accumulation, rounded once. residual may be null, or y itself (an
+ * in-place residual add); y may not overlap x. K * element size must be a multiple of 16 and
+ * the pointers 16-byte aligned. */
+int dkv_linear(const void* x, const void* w, const void* residual, void* y, int32_t rows, int32_t N,
+               int32_t K, int32_t dtype, void* stream);
+
+/* y[r, j] = silu(gate_up[r, j]) * gate_up[r, F + j] with silu(z) = z / (1 + e^-z):
+ * gate_up [rows, 2F] (gate projection, then up projection), y [rows, F]. */
+int dkv_swiglu(const void* gate_up, void* y, int32_t rows, int32_t F, int32_t dtype, void* stream);
+
+/*
  * Streaming read (mode 0) or write (mode 1) of `bytes` bytes of pinned host memory at
  * `host_ptr` by a kernel, the same access path the attention kernels use; measures the
  * host-link rate the layer is bounded by. bytes must be a multiple of 16 * n_wg;

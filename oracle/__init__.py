@@ -157,3 +157,46 @@ def gather_pages(pool, table, n_tokens) -> np.ndarray:
         out[b, :, : len(j), :] = rows.transpose(1, 0, 2)
     return out
 
+
+# ---- a stack of decoder layers around the layer step (the decode loop's surroundings; the
+# pages describe the attention layer only, so these follow the common pre-norm decoder block)
+
+def rmsnorm(x, g, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis, in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(g, dtype=np.float64)
+
+
+def silu(z) -> np.ndarray:
+    """z * sigmoid(z) = z / (1 + e^-z), in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(gu) -> np.ndarray:
+    """silu(gate) * up for gu = [gate, up] side by side on the last axis."""
+    gu = np.asarray(gu, dtype=np.float64)
+    F = gu.shape[-1] // 2
+    return silu(gu[..., :F]) * gu[..., F:]
+
+
+def decode_stack_step(h, layers, caches, past_len, n_q_heads: int, dtype: str, eps: float) -> np.ndarray:
+    """One decode step of a stack of pre-norm decoder layers on hidden states h [B, D]:
+    h <- h + attn(rmsnorm(h)) @ Wo;  h <- h + swiglu(rmsnorm(h) @ W_gu) @ W_down.
+    layers: dicts of [in, out] weights (wq, wk, wv, wo, w_gu, w_down, g_attn, g_mlp);
+    caches: one (kc, vc) pair per layer, appended to in place. Every tensor the GPU stores
+    between kernels (each norm output, the attention output, each residual sum, the MLP's
+    gate-up product and activation) is rounded to `dtype` here at the same points."""
+    h = round_to_dtype(h, dtype)
+    B, D = h.shape
+    for lw, (kc, vc) in zip(layers, caches):
+        a = round_to_dtype(rmsnorm(h, lw["g_attn"], eps), dtype)
+        o = layer_step(a[:, None, :], lw["wq"], lw["wk"], lw["wv"], kc, vc, past_len, n_q_heads, dtype)
+        o = round_to_dtype(o.reshape(B, -1), dtype)
+        h = round_to_dtype(h + project(o, lw["wo"]), dtype)
+        m = round_to_dtype(rmsnorm(h, lw["g_mlp"], eps), dtype)
+        gu = round_to_dtype(project(m, lw["w_gu"]), dtype)
+        act = round_to_dtype(swiglu(gu), dtype)
+        h = round_to_dtype(h + project(act, lw["w_down"]), dtype)
+    return h
+

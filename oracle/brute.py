@@ -88,3 +88,36 @@ def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads, dtype):
                 for i in range(d):
                     out[b][t][h][i] = math.fsum(w[j] * vc[b][g][j][i] for j in range(nk)) / l
     return out
+
+
+def decode_stack_step(h, layers, caches, past_len, n_q_heads, dtype, eps):
+    """The decoder-stack decode step of `oracle.decode_stack_step`, for tiny shapes, with plain
+    loops: h nested [B][D]; layers: dicts of nested [in][out] weight lists and [D] norm weights;
+    caches: per layer (kc, vc) nested lists (modified in place). Every stored tensor is rounded
+    exactly (representable_round of the correctly rounded float value), at the same points.
+    Returns h as nested floats."""
+    def rnd(v):
+        return float(representable_round(_frac(v), dtype))
+
+    def norm(row, g):
+        ms = math.fsum(v * v for v in row) / len(row)
+        s = math.sqrt(ms + eps)
+        return [rnd(row[i] / s * g[i]) for i in range(len(row))]
+
+    def matvec(row, w):      # row [K] times w [K][N], exact, then rounded once
+        K, N = len(w), len(w[0])
+        return [sum((_frac(row[k]) * _frac(w[k][n]) for k in range(K)), Fraction(0)) for n in range(N)]
+
+    h = [[rnd(v) for v in row] for row in h]
+    B = len(h)
+    for lw, (kc, vc) in zip(layers, caches):
+        a = [norm(h[b], lw["g_attn"]) for b in range(B)]
+        o = layer_step([[a[b]] for b in range(B)], lw["wq"], lw["wk"], lw["wv"], kc, vc, past_len, n_q_heads, dtype)
+        o = [[rnd(v) for head in o[b][0] for v in head] for b in range(B)]
+        h = [[rnd(_frac(h[b][n]) + p) for n, p in enumerate(matvec(o[b], lw["wo"]))] for b in range(B)]
+        m = [norm(h[b], lw["g_mlp"]) for b in range(B)]
+        gu = [[rnd(v) for v in matvec(m[b], lw["w_gu"])] for b in range(B)]
+        F = len(gu[0]) // 2
+        act = [[rnd(gu[b][j] / (1.0 + math.exp(-gu[b][j])) * gu[b][F + j]) for j in range(F)] for b in range(B)]
+        h = [[rnd(_frac(h[b][n]) + p) for n, p in enumerate(matvec(act[b], lw["w_down"]))] for b in range(B)]
+    return h

@@ -148,6 +148,24 @@ def layer_weights(draw: Draw, D: int, Hq: int, Hkv: int, d: int, dtype: str):
     return wq, wk, wv
 
 
+def stack_weights(draw: Draw, n_layers: int, D: int, Hq: int, Hkv: int, d: int, F: int, dtype: str):
+    """Weights of a stack of pre-norm decoder layers, all stored [in, out] and used as X @ W,
+    drawn layer by layer in this order: Wq, Wk, Wv [D, H·d] ~ N(0, 1/D); Wo [Hq·d, D] ~
+    N(0, 1/(Hq·d)); the gate and up projections side by side, W_gu [D, 2F] ~ N(0, 1/D); W_down
+    [F, D] ~ N(0, 1/F); the two norm weights g_attn, g_mlp [D] ~ 1 + N(0, 0.1^2)."""
+    layers = []
+    for _ in range(n_layers):
+        wq, wk, wv = layer_weights(draw, D, Hq, Hkv, d, dtype)
+        layers.append(dict(
+            wq=wq, wk=wk, wv=wv,
+            wo=draw.weights(Hq * d, D, dtype),
+            w_gu=draw.weights(D, 2 * F, dtype),
+            w_down=draw.weights(F, D, dtype),
+            g_attn=quantize(1.0 + draw.normal((D,), 0.1, "f32"), dtype),
+            g_mlp=quantize(1.0 + draw.normal((D,), 0.1, "f32"), dtype)))
+    return layers
+
+
 def fill_past(draw: Draw, kc: np.ndarray, vc: np.ndarray, past_len, dtype: str) -> None:
     """Write N(0, 1) past K (all slices) then past V into rows [0, past_len[b]) of
     caches shaped [B, Hkv, cap, d]. `kc`/`vc` may be float32 arrays or storage views."""

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 from oracle import brute
+import synth
 from synth import Draw, quantize
 
 DTYPES = ["f32", "f16", "bf16"]
@@ -397,3 +398,73 @@ def test_paged_layer_step_equals_contiguous_layer_step():
     got = oracle.layer_step(x, wq, wk, wv, kg, vg, past, 4, "bf16")
     assert np.array_equal(got, want)
     assert max(n_tok) <= cap
+
+
+# ---- decoder-stack pieces around the layer (RMSNorm, SiLU/SwiGLU, the stack step)
+
+def test_rmsnorm_closed_forms():
+    # a constant row c·1 with unit weights: every output is c / sqrt(c^2 + eps)
+    c, eps = -3.0, 1e-5
+    out = oracle.rmsnorm(np.full((1, 8), c), np.ones(8), eps)
+    np.testing.assert_allclose(out, c / np.sqrt(c * c + eps), rtol=1e-15)
+    # eps = 0: scale invariant, unit mean square, and the weight multiplies elementwise
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((3, 16))
+    g = rng.standard_normal(16)
+    y = oracle.rmsnorm(x, np.ones(16), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.rmsnorm(7.5 * x, g, 0.0), oracle.rmsnorm(x, g, 0.0), rtol=1e-14)
+    np.testing.assert_allclose(oracle.rmsnorm(x, g, 0.0), y * g, rtol=1e-14)
+
+
+def test_silu_and_swiglu_identities():
+    z = np.linspace(-20.0, 20.0, 401)
+    s = oracle.silu(z)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(s - oracle.silu(-z), z, atol=1e-12)        # silu(z) - silu(-z) = z
+    np.testing.assert_allclose(oracle.silu(np.array([40.0])), 40.0, rtol=1e-15)
+    np.testing.assert_allclose(oracle.silu(np.array([np.log(3.0)])), np.log(3.0) * 0.75, rtol=1e-15)  # sigmoid(ln 3) = 3/4
+    gate, up = z[:200].reshape(2, 100), z[200:400].reshape(2, 100)
+    np.testing.assert_allclose(oracle.swiglu(np.concatenate([gate, up], -1)), oracle.silu(gate) * up, rtol=1e-15)
+
+
+def _tiny_stack(seed, dtype, n_layers=2, B=2, D=16, Hq=4, Hkv=2, d=4, F=8, past=(3, 6)):
+    dr = Draw(seed)
+    layers = synth.stack_weights(dr, n_layers, D, Hq, Hkv, d, F, dtype)
+    cap = max(past) + 2
+    caches = []
+    for _ in range(n_layers):
+        kc = np.zeros((B, Hkv, cap, d), dtype=np.float32)
+        vc = np.zeros((B, Hkv, cap, d), dtype=np.float32)
+        synth.fill_past(dr, kc, vc, past, dtype)
+        caches.append((kc, vc))
+    h = dr.normal((B, D), 1.0, dtype)
+    return layers, caches, h, np.array(past, dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_stack_step_matches_brute_force(dtype):
+    layers, caches, h, past = _tiny_stack(51, dtype)
+    bl = [{k: (v.astype(np.float64).tolist()) for k, v in lw.items()} for lw in layers]
+    bc = [(kc.astype(np.float64).tolist(), vc.astype(np.float64).tolist()) for kc, vc in caches]
+    got = oracle.decode_stack_step(h, layers, caches, past, 4, dtype, 1e-5)
+    ref = np.array(brute.decode_stack_step(h.astype(np.float64).tolist(), bl, bc, [int(p) for p in past], 4,
+                                           dtype, 1e-5))
+    # both round every stored tensor to dtype; fp64 vs exact sums can only flip a rounding at a
+    # tie-near boundary, which this seed does not hit
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    for (kc, vc), (bk, bv) in zip(caches, bc):           # both appended the same rows
+        assert np.array_equal(kc.astype(np.float64), np.array(bk))
+        assert np.array_equal(vc.astype(np.float64), np.array(bv))
+
+
+def test_decode_stack_with_zero_output_weights_keeps_h():
+    # Wo = W_down = 0: both residual branches add nothing, the caches still get the new row
+    layers, caches, h, past = _tiny_stack(52, "f32", n_layers=1)
+    layers[0]["wo"][:] = 0.0
+    layers[0]["w_down"][:] = 0.0
+    before = caches[0][0].copy()
+    got = oracle.decode_stack_step(h, layers, caches, past, 4, "f32", 1e-5)
+    assert np.array_equal(got, h.astype(np.float64))
+    for b, L in enumerate(past):
+        assert not np.array_equal(caches[0][0][b, :, L], before[b, :, L])

@@ -23,7 +23,7 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HO
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
            "attn_prefill_variant", "attn_decode", "attn_decode_variant", "kv_paged_alloc_host", "kv_paged_free_host",
            "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
-           "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+           "dkv_rmsnorm", "dkv_linear", "dkv_swiglu", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
 PAGE_TOKENS = 16
 PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2, "staged": 3}
 DECODE_VARIANTS = {"zerocopy": 0, "staged": 1}
@@ -81,12 +81,16 @@ def lib() -> ctypes.CDLL:
                                          I32, VP, VP, SZ, VP]
         L.attn_decode_paged.argtypes = [P(dkv_paged_cache), P(I32), I32, VP, VP, VP, VP, P(I32), I32, I32, I32,
                                         VP, VP, SZ, VP]
+        L.dkv_rmsnorm.argtypes = [VP, VP, VP, I32, I32, ctypes.c_float, I32, VP]
+        L.dkv_linear.argtypes = [VP, VP, VP, VP, I32, I32, I32, I32, VP]
+        L.dkv_swiglu.argtypes = [VP, VP, I32, I32, I32, VP]
         L.dkv_hostlink_stream.argtypes = [VP, SZ, I32, I32, VP]
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
         for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
                      "attn_decode", "attn_decode_variant", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
-                     "attn_prefill_paged", "attn_decode_paged", "dkv_hostlink_stream"):
+                     "attn_prefill_paged", "attn_decode_paged", "dkv_rmsnorm", "dkv_linear", "dkv_swiglu",
+                     "dkv_hostlink_stream"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -329,6 +333,34 @@ def attn_decode_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: 
     _check(lib().attn_decode_variant(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
                                      n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream),
                                      DECODE_VARIANTS[variant]))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[t.dtype]
+
+
+def rmsnorm(x, weight, y, eps: float = 1e-5, stream=None) -> None:
+    """y = x / sqrt(mean(x^2) + eps) * weight over the last axis; y may be x."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    _check(lib().dkv_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), rows, D, eps, _dtype_code(x), _stream(stream)))
+
+
+def linear(x, w, y, residual=None, stream=None) -> None:
+    """y = x @ w.T (+ residual); w is a [out, in] weight; residual may be y itself."""
+    K = x.shape[-1]
+    rows = x.numel() // K
+    N = w.shape[0]
+    _check(lib().dkv_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), rows, N, K, _dtype_code(x),
+                            _stream(stream)))
+
+
+def swiglu(gate_up, y, stream=None) -> None:
+    """y = silu(gate) * up for gate_up = [gate, up] on the last axis."""
+    F2 = gate_up.shape[-1]
+    rows = gate_up.numel() // F2
+    _check(lib().dkv_swiglu(_ptr(gate_up), _ptr(y), rows, F2 // 2, _dtype_code(gate_up), _stream(stream)))
 
 
 def hostlink_stream(host_ptr: int, nbytes: int, mode: str, n_wg: int = 1024, stream=None) -> None:

@@ -793,6 +793,62 @@ int attn_prefill_paged(const dkv_paged_cache* c, const int32_t* block_table, int
                      DKV_PREFILL_FUSED);
 }
 
+// ---- decode-loop helpers
+
+namespace {
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+int check_dtype(int32_t dtype) {
+  return (dtype < DKV_F32 || dtype > DKV_BF16) ? fail(DKV_ERR_UNSUPPORTED, "dtype %d", dtype) : DKV_OK;
+}
+}  // namespace
+
+int dkv_rmsnorm(const void* x, const void* weight, void* y, int32_t rows, int32_t D, float eps, int32_t dtype,
+                void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (!x || !weight || !y) return fail(DKV_ERR_INVALID_ARG, "a pointer is null");
+  if (rows <= 0 || D <= 0) return fail(DKV_ERR_INVALID_ARG, "rows and D must be positive");
+  if (!(eps >= 0.f)) return fail(DKV_ERR_INVALID_ARG, "eps must be >= 0");
+  const size_t e = elem_size(dtype);
+  if (x != y && overlaps(x, (size_t)rows * D * e, y, (size_t)rows * D * e))
+    return fail(DKV_ERR_INVALID_ARG, "y overlaps x without being x");
+  hipError_t err = launch_rmsnorm(dtype, x, weight, y, rows, D, eps, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? DKV_OK : hip_fail(err, "rmsnorm launch");
+}
+
+int dkv_linear(const void* x, const void* w, const void* residual, void* y, int32_t rows, int32_t N, int32_t K,
+               int32_t dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (!x || !w || !y) return fail(DKV_ERR_INVALID_ARG, "a pointer is null");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(DKV_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (rows <= 0 || N <= 0 || K <= 0) return fail(DKV_ERR_INVALID_ARG, "rows, N and K must be positive");
+  const size_t e = elem_size(dtype);
+  if ((K * e) % 16 != 0) return fail(DKV_ERR_INVALID_ARG, "K=%d: rows of x and w must be whole 16-byte units", K);
+  const size_t ny = (size_t)rows * N * e;
+  if (overlaps(x, (size_t)rows * K * e, y, ny)) return fail(DKV_ERR_INVALID_ARG, "y overlaps x");
+  if (residual && residual != y && overlaps(residual, ny, y, ny))
+    return fail(DKV_ERR_INVALID_ARG, "y overlaps the residual without being it");
+  hipError_t err = launch_linear(dtype, x, w, residual, y, rows, N, K, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? DKV_OK : hip_fail(err, "linear launch");
+}
+
+int dkv_swiglu(const void* gate_up, void* y, int32_t rows, int32_t F, int32_t dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (!gate_up || !y) return fail(DKV_ERR_INVALID_ARG, "a pointer is null");
+  if (rows <= 0 || F <= 0) return fail(DKV_ERR_INVALID_ARG, "rows and F must be positive");
+  const size_t e = elem_size(dtype);
+  if (overlaps(gate_up, (size_t)rows * 2 * F * e, y, (size_t)rows * F * e))
+    return fail(DKV_ERR_INVALID_ARG, "y overlaps gate_up");
+  hipError_t err = launch_swiglu(dtype, gate_up, y, rows, F, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? DKV_OK : hip_fail(err, "swiglu launch");
+}
+
 int dkv_hostlink_stream(void* host_ptr, size_t bytes, int32_t mode, int32_t n_wg, void* stream) {
   if (!host_ptr || !aligned16(host_ptr)) return fail(DKV_ERR_INVALID_ARG, "host_ptr null or misaligned");
   if (mode != 0 && mode != 1) return fail(DKV_ERR_INVALID_ARG, "mode must be 0 (read) or 1 (write)");

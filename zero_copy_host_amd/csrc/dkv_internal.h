@@ -198,4 +198,11 @@ size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G);
 
 hipError_t launch_hostlink(void* p, size_t bytes, int mode, int n_wg, hipStream_t s);
 
+// decode-loop kernels around the layer (model.hip); dtype as dkv_dtype
+hipError_t launch_rmsnorm(int dtype, const void* x, const void* w, void* y, int rows, int D, float eps,
+                          hipStream_t s);
+hipError_t launch_linear(int dtype, const void* x, const void* w, const void* res, void* y, int rows, int N, int K,
+                         hipStream_t s);
+hipError_t launch_swiglu(int dtype, const void* gu, void* y, int rows, int F, hipStream_t s);
+
 }  // namespace dkv
