@@ -140,8 +140,10 @@ PREFILL_CASES = [
     (2, 200, [100, 300], 512, 8, 2, 128, "bf16"),
     (2, 77, [0, 1029], 256, 16, 2, 64, "f16"),       # G = 8, ragged tail
     (1, 300, [5000], 256, 4, 1, 128, "bf16"),        # two key super-chunks
-    (2, 300, [3000, 4500], 512, 32, 8, 128, "bf16"),  # three super-chunks, 2 pairs per XCD
+    (2, 300, [3000, 4500], 512, 32, 8, 128, "bf16"),  # 16 pairs: two groups of 8, super-chunks each
     (1, 130, [70], 256, 8, 4, 128, "f32"),
+    (3, 150, [900, 0, 2500], 256, 16, 8, 64, "f16"),  # 24 pairs: three groups of 8
+    (3, 100, [500, 0, 2200], 256, 8, 4, 64, "bf16"),  # 12 pairs: one launch group, 2 pairs per XCD
 ]
 
 

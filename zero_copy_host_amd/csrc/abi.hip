@@ -162,7 +162,7 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
 // during one launch must fit about half of that XCD's 4 MB L2 (a quarter for a paged cache:
 // its super-chunk is scattered over the pool in 4 KB (page, head) blocks, which at half the
 // L2 conflict-miss and are fetched again, 1.28x the host bytes against 1.02x at a quarter)
-int superchunk_keys(const dkv_cache* c, int32_t batch, bool paged) {
+int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged) {
   // a paged launch stages the page ids of its keys in LDS: at most kPagedSuperchunk keys
   const size_t limit = paged ? kPagedSuperchunk : 1 << 20;
   // tuning override (keys, multiple of 64)
@@ -170,7 +170,6 @@ int superchunk_keys(const dkv_cache* c, int32_t batch, bool paged) {
     const long v = strtol(env, nullptr, 10);
     if (v >= 64) return (int)std::min<size_t>(v / 64 * 64, limit);
   }
-  const int pairs = batch * c->n_kv_heads;
   const int per_xcd = std::max(1, (pairs + 7) / 8);
   const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);  // K and V
   size_t keys = ((size_t)(paged ? 1 : 2) << 20) / ((size_t)per_xcd * row_bytes);
@@ -343,53 +342,68 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   aa.max_pages = pg.max_pages;
   const int rows = attn_rows_per_tile();
   aa.q_tiles = (T * G + rows - 1) / rows;
-  aa.xcd_group = variant != DKV_PREFILL_NAIVE && batch * c->n_kv_heads >= 8;
+  const int P = batch * c->n_kv_heads;
+  aa.xcd_group = variant != DKV_PREFILL_NAIVE && P >= 8;
   aa.new_from_host = separate;
-  int max_keys = 0;
-  for (int b = 0; b < batch; ++b) {
-    aa.past_len[b] = past_len[b];
-    max_keys = std::max(max_keys, past_len[b] + T);
-  }
-  // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
-  const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, batch, paged);
-  const int nsc = (max_keys + sk - 1) / sk;
-  // The new rows' host copies are written by launches whose keys hold no host rows (no
-  // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
-  // super-chunk from L2; with no such launch, the last one writes them all. The rows are
-  // split among those launches in proportion to their attention work.
-  int max_past = 0;
-  for (int b = 0; b < batch; ++b) max_past = std::max(max_past, past_len[b]);
-  int first_free = nsc - 1;
-  for (int i = 0; i < nsc; ++i)
-    if (i * sk >= max_past) { first_free = i; break; }
-  auto launch_work = [&](int i) {
-    long long wk_ = 0;
-    for (int b = 0; b < batch; ++b) wk_ += visible_keys(past_len[b], T, i * sk, std::min((i + 1) * sk, max_keys));
-    return wk_;
-  };
-  long long work_total = 0;
-  for (int i = first_free; i < nsc; ++i) work_total += launch_work(i);
-  const long long new_rows = (long long)batch * c->n_kv_heads * T;
-  long long work_before = 0;
-  for (int i = 0; i < nsc; ++i) {
-    aa.kc0 = i * sk;
-    aa.kc1 = std::min((i + 1) * sk, max_keys);
-    aa.first = i == 0;
-    aa.last = i == nsc - 1;
-    aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
-    if (aa.store_new) {
-      const long long wl = launch_work(i);
-      if (work_total > 0) {
-        aa.store_lo = (int)(new_rows * work_before / work_total);
-        aa.store_hi = (int)(new_rows * (work_before + wl) / work_total);
-      } else {
-        aa.store_lo = (int)(new_rows * (i - first_free) / (nsc - first_free));
-        aa.store_hi = (int)(new_rows * (i - first_free + 1) / (nsc - first_free));
-      }
-      work_before += wl;
+  for (int b = 0; b < batch; ++b) aa.past_len[b] = past_len[b];
+  // With a multiple of 8 pairs, the pairs go in groups of 8, one pair per XCD: each XCD's L2
+  // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which
+  // halves the launches every query tile makes and the running-state traffic they cost.
+  const int group = aa.xcd_group && P % 8 == 0 ? 8 : P;
+  for (int pair0 = 0; pair0 < P; pair0 += group) {
+    aa.pair0 = pair0;
+    aa.pairs = group;
+    const int b0 = pair0 / c->n_kv_heads, b1 = (pair0 + group - 1) / c->n_kv_heads;   // sequences served
+    // pairs of sequence b in this group
+    auto npairs = [&](int b) {
+      return std::min((b + 1) * c->n_kv_heads, pair0 + group) - std::max(b * c->n_kv_heads, pair0);
+    };
+    int max_keys = 0, max_past = 0;
+    for (int b = b0; b <= b1; ++b) {
+      max_keys = std::max(max_keys, past_len[b] + T);
+      max_past = std::max(max_past, past_len[b]);
     }
-    e = fa(aa, s);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
+    const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged);
+    const int nsc = (max_keys + sk - 1) / sk;
+    // The new rows' host copies are written by launches whose keys hold no host rows (no
+    // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
+    // super-chunk from L2; with no such launch, the last one writes them all. The rows are
+    // split among those launches in proportion to their attention work.
+    int first_free = nsc - 1;
+    for (int i = 0; i < nsc; ++i)
+      if (i * sk >= max_past) { first_free = i; break; }
+    auto launch_work = [&](int i) {
+      long long wk_ = 0;
+      for (int b = b0; b <= b1; ++b)
+        wk_ += npairs(b) * visible_keys(past_len[b], T, i * sk, std::min((i + 1) * sk, max_keys));
+      return wk_;
+    };
+    long long work_total = 0;
+    for (int i = first_free; i < nsc; ++i) work_total += launch_work(i);
+    const long long new_rows = (long long)group * T;       // (pair, token) rows of this group
+    const long long row0 = (long long)pair0 * T;
+    long long work_before = 0;
+    for (int i = 0; i < nsc; ++i) {
+      aa.kc0 = i * sk;
+      aa.kc1 = std::min((i + 1) * sk, max_keys);
+      aa.first = i == 0;
+      aa.last = i == nsc - 1;
+      aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
+      if (aa.store_new) {
+        const long long wl = launch_work(i);
+        if (work_total > 0) {
+          aa.store_lo = (int)(row0 + new_rows * work_before / work_total);
+          aa.store_hi = (int)(row0 + new_rows * (work_before + wl) / work_total);
+        } else {
+          aa.store_lo = (int)(row0 + new_rows * (i - first_free) / (nsc - first_free));
+          aa.store_hi = (int)(row0 + new_rows * (i - first_free + 1) / (nsc - first_free));
+        }
+        work_before += wl;
+      }
+      e = fa(aa, s);
+      if (e != hipSuccess) return hip_fail(e, "attention launch");
+    }
   }
   return DKV_OK;
 }

@@ -35,6 +35,12 @@ namespace dkv {
 #ifndef DKV_ATTN_SETPRIO
 #define DKV_ATTN_SETPRIO 0
 #endif
+#ifndef DKV_ATTN_KPAD
+#define DKV_ATTN_KPAD 8    // elements of padding per K tile row (16-bit types)
+#endif
+#ifndef DKV_ATTN_VPAD
+#define DKV_ATTN_VPAD 16   // elements of padding per row-major V tile row (16-bit types)
+#endif
 
 template <typename T, int DH>
 struct AttnCfg {
@@ -44,11 +50,11 @@ struct AttnCfg {
   static constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
   static constexpr int EB = sizeof(T);
   static constexpr int VEC = 16 / EB;
-  static constexpr int LDK = DH + VEC;           // K tile row (elements), padded
+  static constexpr int LDK = DH + (EB == 2 ? DKV_ATTN_KPAD : VEC);   // K tile row (elements), padded
   // 16-bit types keep V row-major ([key][d]) and read Vᵀ fragments with the gfx950 LDS
   // transpose read; fp32 stores Vᵀ ([d][key]) at load time instead.
   static constexpr bool VROW = EB == 2;
-  static constexpr int LDV = VROW ? DH + 16 : KT + 16 / EB;
+  static constexpr int LDV = VROW ? DH + DKV_ATTN_VPAD : KT + 16 / EB;
   static constexpr int KTILE = KT * LDK;
   static constexpr int VTILE = VROW ? KT * LDV : DH * LDV;
   static constexpr int CPR = DH / VEC;           // 16-byte chunks per key row
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int half = lane >> 5, col = lane & 31;
 
-  const int P = a.B * a.Hkv;
+  const int P = a.pairs;                         // pairs served by this launch, from a.pair0
   if (a.store_new) {
     // storer role: this step's new K/V rows go from their device copy to the host cache.
     // The host hands each storing launch a share of the (pair, token) rows, [store_lo,
@@ -107,11 +113,12 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
   if (a.xcd_group) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int ppx = (P + 7) >> 3;
-    p = (slot % ppx) * 8 + xcd;
+    const int lp = (slot % ppx) * 8 + xcd;
     qt = a.q_tiles - 1 - slot / ppx;
-    if (p >= P) return;
+    if (lp >= P) return;
+    p = a.pair0 + lp;
   } else {
-    p = blockIdx.x % P;
+    p = a.pair0 + blockIdx.x % P;
     qt = a.q_tiles - 1 - blockIdx.x / P;
   }
   const int b = p / a.Hkv, g = p - b * a.Hkv;
@@ -191,169 +198,163 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       krow[i] = c / CPR;
       off[i] = krow[i] * DH + (c % CPR) * VEC;
     }
-    uint4 rk[LOADS], rv[LOADS];
-    auto gload = [&](int j0) {
-      if (j0 + KT <= key_hi && (j0 + KT <= host_end || j0 >= host_end)) {
-        // whole tile from one source: one uniform base, per-lane offsets
-        const bool host = j0 + KT <= host_end;
-        if (PAGED && host) {
+    // Two register sets: the loads of tile i + 2 are issued while tile i computes, so each
+    // has two tiles of compute to arrive in. Loads are unconditional (a row past the launch's
+    // keys reads the last key row instead, always in bounds) and the zero fill for such rows
+    // happens at the LDS store, which waits for the data anyway: a masked load into pre-zeroed
+    // registers would make the wave wait for its loads right after issuing them.
+    uint4 rk[2][LOADS], rv[2][LOADS];
+    auto gload = [&](int set, int j0) {
 #pragma unroll
-          for (int i = 0; i < LOADS; ++i) {
-            const size_t r = hrow(j0 + krow[i]) + (off[i] - krow[i] * DH);
-            rk[i] = *reinterpret_cast<const uint4*>(kh + r);
-            rv[i] = *reinterpret_cast<const uint4*>(vh + r);
-          }
-        } else {
-          const T* kb0 = host ? kh + (size_t)j0 * DH : kn + (size_t)(j0 - L) * DH;
-          const T* vb0 = host ? vh + (size_t)j0 * DH : vn + (size_t)(j0 - L) * DH;
-#pragma unroll
-          for (int i = 0; i < LOADS; ++i) {
-            rk[i] = *reinterpret_cast<const uint4*>(kb0 + off[i]);
-            rv[i] = *reinterpret_cast<const uint4*>(vb0 + off[i]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int j = j0 + krow[i];
-          const int e = off[i] - krow[i] * DH;
-          if (j < key_hi) {
-            const bool host = j < host_end;
-            const T* ks = host ? kh + hrow(j) : kn + (size_t)(j - L) * DH;
-            const T* vs = host ? vh + hrow(j) : vn + (size_t)(j - L) * DH;
-            rk[i] = *reinterpret_cast<const uint4*>(ks + e);
-            rv[i] = *reinterpret_cast<const uint4*>(vs + e);
-          } else {
-            rk[i] = make_uint4(0, 0, 0, 0);
-            rv[i] = make_uint4(0, 0, 0, 0);
-          }
-        }
+      for (int i = 0; i < LOADS; ++i) {
+        const int j = min(j0 + krow[i], key_hi - 1);
+        const int e = off[i] - krow[i] * DH;
+        const bool host = j < host_end;
+        const T* ks = host ? kh + hrow(j) : kn + (size_t)(j - L) * DH;
+        const T* vs = host ? vh + hrow(j) : vn + (size_t)(j - L) * DH;
+        rk[set][i] = *reinterpret_cast<const uint4*>(ks + e);
+        rv[set][i] = *reinterpret_cast<const uint4*>(vs + e);
       }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, int set, int j0) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int kr = krow[i], kc = off[i] - kr * DH;
-        *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = rk[i];
+        const bool valid = j0 + kr < key_hi;
+        const uint4 kz = valid ? rk[set][i] : make_uint4(0, 0, 0, 0);
+        const uint4 vz = valid ? rv[set][i] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = kz;
         if constexpr (C::VROW) {
-          *reinterpret_cast<uint4*>(&sV[buf][kr * LDV + kc]) = rv[i];
+          *reinterpret_cast<uint4*>(&sV[buf][kr * LDV + kc]) = vz;
         } else {
-          const T* ve = reinterpret_cast<const T*>(&rv[i]);
+          const T* ve = reinterpret_cast<const T*>(&vz);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) sV[buf][(kc + e) * LDV + kr] = ve[e];
         }
       }
     };
 
-    gload(key_lo);
-    sstore(0);
-    __syncthreads();
-    int buf = 0;
-    for (int j0 = key_lo; j0 < key_hi; j0 += KT) {
-      const bool more = j0 + KT < key_hi;
-      if (more) gload(j0 + KT);
-      const T* tK = sK[buf];
-      const T* tV = sV[buf];
-      // Sᵀ for the whole tile: KT/32 blocks of 32 keys x 32 queries
-      f32x16 s[KT / 32];
-      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    // one key tile (KT keys from j0, in LDS buffer buf) against this wave's 32 query rows
+    auto tile = [&](const int j0, const int buf) {
+        const T* tK = sK[buf];
+        const T* tV = sV[buf];
+        // Sᵀ for the whole tile: KT/32 blocks of 32 keys x 32 queries
+        f32x16 s[KT / 32];
+        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb) {
+        for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+          for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < DH / KSTEP; ++ks) {
-          const typename MF::frag ka =
-              *reinterpret_cast<const typename MF::frag*>(tK + (kb * 32 + col) * LDK + ks * KSTEP + half * KPL);
-          s[kb] = MF::mma(ka, qf[ks], s[kb]);
+          for (int ks = 0; ks < DH / KSTEP; ++ks) {
+            const typename MF::frag ka =
+                *reinterpret_cast<const typename MF::frag*>(tK + (kb * 32 + col) * LDK + ks * KSTEP + half * KPL);
+            s[kb] = MF::mma(ka, qf[ks], s[kb]);
+          }
         }
-      }
-      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-      // mask only where some row of this workgroup cannot see some key of the tile
-      const bool need_mask = (j0 + KT > key_hi) || (j0 + KT > key_all);
-      if (need_mask) {
+        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        // mask only where some row of this workgroup cannot see some key of the tile
+        const bool need_mask = (j0 + KT > key_hi) || (j0 + KT > key_all);
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int j = j0 + kb * 32 + acc_row(v, lane);
+              if (j >= key_hi || j > qpos) s[kb][v] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+        // lazy reference maximum: raise it only when a score exceeds it by more than 2^8
+        const bool raise = mx > m_run + kLazyRescale;
+        if (__any(raise)) {
+          const float m_new = raise ? mx : m_run;
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        }
+        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+        float ps = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int j = j0 + kb * 32 + acc_row(v, lane);
-            if (j >= key_hi || j > qpos) s[kb][v] = -INFINITY;
+            s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mref));
+            ps += s[kb][v];
           }
-      }
-      float mx = -INFINITY;
+        l_run += ps + __shfl_xor(ps, 32, 64);
+        // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in
+        // accumulator register stp*KPL + e of that half
+        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb)
+        for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-      // lazy reference maximum: raise it only when a score exceeds it by more than 2^8
-      const bool raise = mx > m_run + kLazyRescale;
-      if (__any(raise)) {
-        const float m_new = raise ? mx : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mref));
-          ps += s[kb][v];
-        }
-      l_run += ps + __shfl_xor(ps, 32, 64);
-      // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in
-      // accumulator register stp*KPL + e of that half
-      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb) {
-#pragma unroll
-        for (int stp = 0; stp < 32 / KSTEP; ++stp) {
-          typename MF::frag pb;
-          if constexpr (KPL == 1) {
-            pb = s[kb][stp];
-          } else {
-#pragma unroll
-            for (int e = 0; e < KPL; ++e) pb[e] = Elem<T>::from_float(s[kb][stp * KPL + e]);
-          }
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            typename MF::frag va;
-            if constexpr (C::VROW) {
-              // lane needs V[keys 16*stp + 4*half + {0..3}, +8 + ...][d = db*32 + col]. The
-              // transpose read gives result lane i (of 16) value k from source lane 4k + i/4,
-              // element i % 4; so source lane 4k + q of each 16-lane group points at
-              // V[kbase + k][d0 + 4q], with d0 the group's first column.
-              const int li = lane & 15, kk = li >> 2, qq = li & 3;
-              const int d0 = db * 32 + (lane & 16);
-              const int kbase = kb * 32 + 16 * stp + 4 * half;
-              const T* src0 = tV + (kbase + kk) * LDV + d0 + 4 * qq;
-              const T* src1 = src0 + 8 * LDV;
-              typedef short v4s __attribute__((ext_vector_type(4)));
-              const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) v4s*)(src0));
-              const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) v4s*)(src1));
-              __builtin_memcpy(&va, &lo, 8);
-              __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
+          for (int stp = 0; stp < 32 / KSTEP; ++stp) {
+            typename MF::frag pb;
+            if constexpr (KPL == 1) {
+              pb = s[kb][stp];
             } else {
-              const T* vrow = tV + (db * 32 + col) * LDV + kb * 32;
-              va = vrow[acc_row(stp, lane)];
+#pragma unroll
+              for (int e = 0; e < KPL; ++e) pb[e] = Elem<T>::from_float(s[kb][stp * KPL + e]);
             }
-            o[db] = MF::mma(va, pb, o[db]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              typename MF::frag va;
+              if constexpr (C::VROW) {
+                // lane needs V[keys 16*stp + 4*half + {0..3}, +8 + ...][d = db*32 + col]. The
+                // transpose read gives result lane i (of 16) value k from source lane 4k + i/4,
+                // element i % 4; so source lane 4k + q of each 16-lane group points at
+                // V[kbase + k][d0 + 4q], with d0 the group's first column.
+                const int li = lane & 15, kk = li >> 2, qq = li & 3;
+                const int d0 = db * 32 + (lane & 16);
+                const int kbase = kb * 32 + 16 * stp + 4 * half;
+                const T* src0 = tV + (kbase + kk) * LDV + d0 + 4 * qq;
+                const T* src1 = src0 + 8 * LDV;
+                typedef short v4s __attribute__((ext_vector_type(4)));
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s*)(src0));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s*)(src1));
+                __builtin_memcpy(&va, &lo, 8);
+                __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
+              } else {
+                const T* vrow = tV + (db * 32 + col) * LDV + kb * 32;
+                va = vrow[acc_row(stp, lane)];
+              }
+              o[db] = MF::mma(va, pb, o[db]);
+            }
           }
         }
-      }
-      if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-      if (more) sstore(buf ^ 1);
+        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    const int n = (key_hi - key_lo + KT - 1) / KT;     // key tiles in this launch
+    gload(0, key_lo);
+    sstore(0, 0, key_lo);
+    if (n > 1) gload(0, key_lo + KT);
+    if (n > 2) gload(1, key_lo + 2 * KT);
+    __syncthreads();
+    // tile t computes from LDS buffer t % 2; register set 0 carries tiles 1, 3, 5, ... and set 1
+    // tiles 2, 4, 6, ... (loaded two tiles ahead, stored to LDS one tile ahead)
+    for (int t = 0; t < n; t += 2) {
+      tile(key_lo + t * KT, 0);
+      if (t + 1 < n) sstore(1, 0, key_lo + (t + 1) * KT);
+      if (t + 3 < n) gload(0, key_lo + (t + 3) * KT);
       __syncthreads();
-      buf ^= 1;
+      if (t + 1 >= n) break;
+      tile(key_lo + (t + 1) * KT, 1);
+      if (t + 2 < n) sstore(0, 1, key_lo + (t + 2) * KT);
+      if (t + 4 < n) gload(1, key_lo + (t + 4) * KT);
+      __syncthreads();
     }
   }
 
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
 
 template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-  const int P = a.B * a.Hkv;
+  const int P = a.pairs;
   const int grid = a.xcd_group ? 8 * ((P + 7) / 8) * a.q_tiles : P * a.q_tiles;
   hipLaunchKernelGGL((attn_kernel<T, DH, G, PAGED>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
   return hipGetLastError();

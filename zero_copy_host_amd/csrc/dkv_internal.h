@@ -168,6 +168,7 @@ struct AttnArgs {
   float* state;             // running o, m, l (log2 domain) per 32 query rows: see attn_state_bytes
   void* out;                // [B, T, Hq*d]
   int32_t B, T, Hq, Hkv, cap;
+  int32_t pair0, pairs;     // this launch serves (sequence, kv head) pairs [pair0, pair0 + pairs)
   int32_t kc0, kc1;         // super-chunk key range
   int32_t first, last;      // first super-chunk (no state to read) / last (finalise)
   int32_t q_tiles;          // row tiles per (b, g)
