@@ -35,17 +35,24 @@ namespace dkv {
 #ifndef DKV_ATTN_SETPRIO
 #define DKV_ATTN_SETPRIO 0
 #endif
+#ifndef DKV_ATTN_WAVES
+#define DKV_ATTN_WAVES 8   // waves per workgroup, 32 query rows each
+#endif
+#ifndef DKV_ATTN_MINWG
+#define DKV_ATTN_MINWG 1   // workgroups per CU the register allocation must allow
+#endif
 #ifndef DKV_ATTN_KPAD
 #define DKV_ATTN_KPAD 8    // elements of padding per K tile row (16-bit types)
 #endif
 #ifndef DKV_ATTN_VPAD
-#define DKV_ATTN_VPAD 16   // elements of padding per row-major V tile row (16-bit types)
+#define DKV_ATTN_VPAD 32   // elements of padding per row-major V tile row (16-bit types); 32 makes
+                           // the transpose reads of the two 16-lane halves hit disjoint LDS banks
 #endif
 
 template <typename T, int DH>
 struct AttnCfg {
   static constexpr int KT = sizeof(T) == 2 ? DKV_ATTN_KT : 64;   // keys per LDS tile
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = DKV_ATTN_WAVES;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
   static constexpr int EB = sizeof(T);
@@ -70,7 +77,7 @@ constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max pas
 // PAGED: the host cache is a page pool addressed through the block table; the page ids of
 // the launch's host keys are staged in LDS before the sweep.
 template <typename T, int DH, int G, bool PAGED>
-__global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kernel(const AttnArgs a) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
   constexpr int KT = C::KT, VEC = C::VEC, LDK = C::LDK, LDV = C::LDV, LOADS = C::LOADS, DB = C::DB;
@@ -198,32 +205,42 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
       krow[i] = c / CPR;
       off[i] = krow[i] * DH + (c % CPR) * VEC;
     }
-    // Two register sets: the loads of tile i + 2 are issued while tile i computes, so each
-    // has two tiles of compute to arrive in. Loads are unconditional (a row past the launch's
-    // keys reads the last key row instead, always in bounds) and the zero fill for such rows
-    // happens at the LDS store, which waits for the data anyway: a masked load into pre-zeroed
-    // registers would make the wave wait for its loads right after issuing them.
+    // Global -> register loads (gk, gv) and register -> LDS stores (sk, sv) of one key tile.
+    // Loads are unconditional (a row past the launch's keys reads the last key row instead,
+    // always in bounds) and the zero fill for such rows happens at the LDS store, which waits
+    // for the data anyway: a masked load into pre-zeroed registers would make the wave wait
+    // for its loads right after issuing them.
     uint4 rk[2][LOADS], rv[2][LOADS];
-    auto gload = [&](int set, int j0) {
+    auto gk = [&](int set, int j0) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int j = min(j0 + krow[i], key_hi - 1);
         const int e = off[i] - krow[i] * DH;
-        const bool host = j < host_end;
-        const T* ks = host ? kh + hrow(j) : kn + (size_t)(j - L) * DH;
-        const T* vs = host ? vh + hrow(j) : vn + (size_t)(j - L) * DH;
+        const T* ks = j < host_end ? kh + hrow(j) : kn + (size_t)(j - L) * DH;
         rk[set][i] = *reinterpret_cast<const uint4*>(ks + e);
+      }
+    };
+    auto gv = [&](int set, int j0) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int j = min(j0 + krow[i], key_hi - 1);
+        const int e = off[i] - krow[i] * DH;
+        const T* vs = j < host_end ? vh + hrow(j) : vn + (size_t)(j - L) * DH;
         rv[set][i] = *reinterpret_cast<const uint4*>(vs + e);
       }
     };
-    auto sstore = [&](int buf, int set, int j0) {
+    auto sk = [&](int buf, int set, int j0) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int kr = krow[i], kc = off[i] - kr * DH;
-        const bool valid = j0 + kr < key_hi;
-        const uint4 kz = valid ? rk[set][i] : make_uint4(0, 0, 0, 0);
-        const uint4 vz = valid ? rv[set][i] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = kz;
+        *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = j0 + kr < key_hi ? rk[set][i] : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto sv = [&](int buf, int set, int j0) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int kr = krow[i], kc = off[i] - kr * DH;
+        const uint4 vz = j0 + kr < key_hi ? rv[set][i] : make_uint4(0, 0, 0, 0);
         if constexpr (C::VROW) {
           *reinterpret_cast<uint4*>(&sV[buf][kr * LDV + kc]) = vz;
         } else {
@@ -233,118 +250,128 @@ __global__ __launch_bounds__(512) void attn_kernel(const AttnArgs a) {
         }
       }
     };
+    auto gload = [&](int set, int j0) { gk(set, j0); gv(set, j0); };
+    auto sstore = [&](int buf, int set, int j0) { sk(buf, set, j0); sv(buf, set, j0); };
 
-    // one key tile (KT keys from j0, in LDS buffer buf) against this wave's 32 query rows
-    auto tile = [&](const int j0, const int buf) {
-        const T* tK = sK[buf];
-        const T* tV = sV[buf];
-        // Sᵀ for the whole tile: KT/32 blocks of 32 keys x 32 queries
-        f32x16 s[KT / 32];
-        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    // ---- the three parts of a key tile (KT keys) against this wave's 32 query rows
+    typedef f32x16 Scores[KT / 32];                      // Sᵀ: KT/32 blocks of 32 keys x 32 queries
+    typedef typename MF::frag Probs[KT / 32][32 / KSTEP];  // Pᵀ in MFMA operand form
+    auto qk = [&](const T* tK, Scores& sc) {
 #pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb) {
+      for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < DH / KSTEP; ++ks) {
-            const typename MF::frag ka =
-                *reinterpret_cast<const typename MF::frag*>(tK + (kb * 32 + col) * LDK + ks * KSTEP + half * KPL);
-            s[kb] = MF::mma(ka, qf[ks], s[kb]);
-          }
+        for (int ks = 0; ks < DH / KSTEP; ++ks) {
+          const typename MF::frag ka =
+              *reinterpret_cast<const typename MF::frag*>(tK + (kb * 32 + col) * LDK + ks * KSTEP + half * KPL);
+          sc[kb] = MF::mma(ka, qf[ks], ks == 0 ? f32x16{} : sc[kb]);
         }
-        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-        // mask only where some row of this workgroup cannot see some key of the tile
-        const bool need_mask = (j0 + KT > key_hi) || (j0 + KT > key_all);
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int j = j0 + kb * 32 + acc_row(v, lane);
-              if (j >= key_hi || j > qpos) s[kb][v] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-        // lazy reference maximum: raise it only when a score exceeds it by more than 2^8
-        const bool raise = mx > m_run + kLazyRescale;
-        if (__any(raise)) {
-          const float m_new = raise ? mx : m_run;
-          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-        }
-        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-        float ps = 0.f;
+      }
+    };
+    // mask, tile maximum and the lazy raise of the reference maximum (rescaling o and l)
+    auto rebase = [&](const int j0, Scores& sc) {
+      // mask only where some row of this workgroup cannot see some key of the tile
+      if ((j0 + KT > key_hi) || (j0 + KT > key_all)) {
 #pragma unroll
         for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], sl2, -mref));
-            ps += s[kb][v];
+            const int j = j0 + kb * 32 + acc_row(v, lane);
+            if (j >= key_hi || j > qpos) sc[kb][v] = -INFINITY;
           }
-        l_run += ps + __shfl_xor(ps, 32, 64);
-        // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in
-        // accumulator register stp*KPL + e of that half
-        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      }
+      float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb) {
+      for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
-          for (int stp = 0; stp < 32 / KSTEP; ++stp) {
-            typename MF::frag pb;
-            if constexpr (KPL == 1) {
-              pb = s[kb][stp];
-            } else {
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      // lazy reference maximum: raise it only when a score exceeds it by more than 2^8
+      const bool raise = mx > m_run + kLazyRescale;
+      if (__any(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-              for (int e = 0; e < KPL; ++e) pb[e] = Elem<T>::from_float(s[kb][stp * KPL + e]);
-            }
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              typename MF::frag va;
-              if constexpr (C::VROW) {
-                // lane needs V[keys 16*stp + 4*half + {0..3}, +8 + ...][d = db*32 + col]. The
-                // transpose read gives result lane i (of 16) value k from source lane 4k + i/4,
-                // element i % 4; so source lane 4k + q of each 16-lane group points at
-                // V[kbase + k][d0 + 4q], with d0 the group's first column.
-                const int li = lane & 15, kk = li >> 2, qq = li & 3;
-                const int d0 = db * 32 + (lane & 16);
-                const int kbase = kb * 32 + 16 * stp + 4 * half;
-                const T* src0 = tV + (kbase + kk) * LDV + d0 + 4 * qq;
-                const T* src1 = src0 + 8 * LDV;
-                typedef short v4s __attribute__((ext_vector_type(4)));
-                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s*)(src0));
-                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4s*)(src1));
-                __builtin_memcpy(&va, &lo, 8);
-                __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
-              } else {
-                const T* vrow = tV + (db * 32 + col) * LDV + kb * 32;
-                va = vrow[acc_row(stp, lane)];
-              }
-              o[db] = MF::mma(va, pb, o[db]);
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      }
+    };
+    // Pᵀ = exp2(Sᵀ·scale - m) in operand form, and the row sums into l
+    auto probs = [&](const Scores& sc, Probs& pb) {
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+        for (int stp = 0; stp < 32 / KSTEP; ++stp) {
+          if constexpr (KPL == 1) {
+            const float w = __builtin_amdgcn_exp2f(fmaf(sc[kb][stp], sl2, -mref));
+            ps += w;
+            pb[kb][stp] = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) {
+              const float w = __builtin_amdgcn_exp2f(fmaf(sc[kb][stp * KPL + e], sl2, -mref));
+              ps += w;
+              pb[kb][stp][e] = Elem<T>::from_float(w);
             }
           }
         }
-        if (DKV_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      l_run += ps + __shfl_xor(ps, 32, 64);
+    };
+    // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in accumulator
+    // register stp*KPL + e of that half, i.e. element e of pb[kb][stp]
+    auto pv = [&](const T* tV, const Probs& pb) {
+#pragma unroll
+      for (int kb = 0; kb < KT / 32; ++kb) {
+#pragma unroll
+        for (int stp = 0; stp < 32 / KSTEP; ++stp) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            typename MF::frag va;
+            if constexpr (C::VROW) {
+              // lane needs V[keys 16*stp + 4*half + {0..3}, +8 + ...][d = db*32 + col]. The
+              // transpose read gives result lane i (of 16) value k from source lane 4k + i/4,
+              // element i % 4; so source lane 4k + q of each 16-lane group points at
+              // V[kbase + k][d0 + 4q], with d0 the group's first column.
+              const int li = lane & 15, kk = li >> 2, qq = li & 3;
+              const int d0 = db * 32 + (lane & 16);
+              const int kbase = kb * 32 + 16 * stp + 4 * half;
+              const T* src0 = tV + (kbase + kk) * LDV + d0 + 4 * qq;
+              const T* src1 = src0 + 8 * LDV;
+              typedef short v4s __attribute__((ext_vector_type(4)));
+              const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(src0));
+              const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(src1));
+              __builtin_memcpy(&va, &lo, 8);
+              __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
+            } else {
+              const T* vrow = tV + (db * 32 + col) * LDV + kb * 32;
+              va = vrow[acc_row(stp, lane)];
+            }
+            o[db] = MF::mma(va, pb[kb][stp], o[db]);
+          }
+        }
+      }
     };
 
     const int n = (key_hi - key_lo + KT - 1) / KT;     // key tiles in this launch
+    Probs pb;
+    // tile t computes from LDS buffer t % 2; register set 0 carries tiles 1, 3, 5, ... and set 1
+    // tiles 2, 4, 6, ... (loaded two tiles ahead, stored to LDS one tile ahead)
+    Scores sc;
+    auto tile = [&](const int j0, const int buf) {
+      qk(sK[buf], sc);
+      rebase(j0, sc);
+      probs(sc, pb);
+      pv(sV[buf], pb);
+    };
     gload(0, key_lo);
     sstore(0, 0, key_lo);
     if (n > 1) gload(0, key_lo + KT);
     if (n > 2) gload(1, key_lo + 2 * KT);
     __syncthreads();
-    // tile t computes from LDS buffer t % 2; register set 0 carries tiles 1, 3, 5, ... and set 1
-    // tiles 2, 4, 6, ... (loaded two tiles ahead, stored to LDS one tile ahead)
     for (int t = 0; t < n; t += 2) {
       tile(key_lo + t * KT, 0);
       if (t + 1 < n) sstore(1, 0, key_lo + (t + 1) * KT);
@@ -412,7 +439,7 @@ attn_fn find_attn(int dtype, int d, int G, bool paged) {
   }
 }
 
-int attn_rows_per_tile() { return 256; }
+int attn_rows_per_tile() { return 32 * DKV_ATTN_WAVES; }
 
 size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G) {
   const size_t nblk = ((size_t)T * G + 31) / 32;
