@@ -7,23 +7,26 @@
 //
 // gfx950 mapping. The stationary buffer for host KV is an XCD's L2 (4 MB), shared by the
 // 32 CUs of that XCD, rather than one CU's LDS: the host calls this kernel once per key
-// super-chunk [kc0, kc1) sized to fit L2, and workgroup i runs on XCD i % 8, so the query
-// tiles of one (sequence, kv head) pair are placed on one XCD and read the super-chunk from
-// L2 after its first fetch over the link. Everything else a workgroup touches (queries,
-// running state, output) is streamed with non-temporal loads and stores so that it does
-// not push the super-chunk out of L2 between rounds of query tiles. Each workgroup keeps
-// 256 query rows in registers (8 waves x 32), sweeps the super-chunk through a
-// double-buffered LDS tile, and carries the per-row softmax state (o, m, l) in device
-// memory from one super-chunk launch to the next. Keys below past_len[b] come from the host
-// cache; this step's new keys come from the device copy the projection left, so they
-// never cross the link a second time.
+// super-chunk [kc0, kc1) sized to fit L2 (for each group of up to 8 (sequence, kv head)
+// pairs), and workgroup i runs on XCD i % 8, so the query tiles of one pair are placed on
+// one XCD and read the super-chunk from L2 after its first fetch over the link. Everything
+// else a workgroup touches (queries, running state, output) is streamed with non-temporal
+// loads and stores so that it does not push the super-chunk out of L2 between rounds of
+// query tiles. Each workgroup keeps 256 query rows in registers (8 waves x 32), sweeps the
+// super-chunk through double-buffered LDS tiles (loads issued two tiles ahead), and carries
+// the per-row softmax state (o, m, l) in device memory from one super-chunk launch to the
+// next. Keys below past_len[b] come from the host cache; this step's new keys come from the
+// device copy the projection left, so they never cross the link a second time. Launches
+// whose keys hold no host rows also write this step's new rows to the host cache (the
+// storer role), a share each.
 //
 // MFMA layout: scores are computed transposed, Sᵀ = K·Qᵀ (32 keys x 32 queries per block),
 // so each lane owns one query column: row max / sum need one cross-half exchange, the
 // accumulators are reused directly as the Pᵀ operand of Oᵀ += Vᵀ·Pᵀ, and Oᵀ rescaling is
-// lane-local. V is transposed once into LDS when a tile is loaded. The softmax reference
-// maximum is raised lazily (only when a score exceeds it by more than 2^8), so the Oᵀ
-// rescale is skipped by whole waves once the maximum has settled.
+// lane-local. V stays row-major in LDS and the Vᵀ operand is read with the gfx950 LDS
+// transpose read (16-bit types); fp32 stores V transposed. The softmax reference maximum is
+// raised lazily (only when a score exceeds it by more than 2^8), so the Oᵀ rescale is
+// skipped by whole waves once the maximum has settled.
 #include "dkv_internal.h"
 
 namespace dkv {
