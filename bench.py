@@ -153,6 +153,22 @@ def _layer_setup(dkv, w, seed_extra=0):
     return past, cache, dev, dr
 
 
+KEY_TILE = 64   # keys per tile of one (sequence, kv head) stream in both attention kernels
+
+
+def _overlap_model(new_tokens, past, host_read, flops, peak_tflops, ms, peak_read):
+    """The pages' two-stage pipeline model of the step as an expected time: the longest
+    (sequence, kv head) key stream in 64-key tiles, its transfer at the measured link read peak
+    and its compute at the dtype's dense MFMA peak."""
+    from zero_copy_host_amd import accounting as acc
+    if not peak_read:
+        return None
+    n_tiles = -(-(int(np.max(past)) + new_tokens) // KEY_TILE)
+    expected = acc.overlap_model_seconds(n_tiles, host_read, flops, peak_read * 1e9, peak_tflops * 1e12) * 1e3
+    return {"expected_ms": expected, "n_tiles": n_tiles, "link_GBps": peak_read, "compute_tflops": peak_tflops,
+            "measured_over_expected": ms / expected if expected else None}
+
+
 def _prefill_stats(w, past, ms, peak_read):
     import synth
     from zero_copy_host_amd import accounting as acc
@@ -166,7 +182,8 @@ def _prefill_stats(w, past, ms, peak_read):
             "tflops": tflops, "mfma_peak_tflops": mfma_peak, "mfma_frac": tflops / mfma_peak,
             "host_read_bytes": host_read, "host_write_bytes": host_write,
             "host_read_floor_ms": host_read / (peak_read * 1e9) * 1e3 if peak_read else None,
-            "mfma_floor_ms": flops / (mfma_peak * 1e12) * 1e3}
+            "mfma_floor_ms": flops / (mfma_peak * 1e12) * 1e3,
+            "overlap_model": _overlap_model(w.T, past, host_read, flops, mfma_peak, ms, peak_read)}
 
 
 def _decode_stats(w, past, ms, peak_read):
@@ -175,9 +192,11 @@ def _decode_stats(w, past, ms, peak_read):
     e = synth.elem_bytes(w.dtype)
     host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)
     gbps = host_read / (ms * 1e-3) / 1e9
+    flops = acc.attention_flops(past, 1, w.Hq, w.d) + acc.projection_flops(w.B, 1, w.D, w.Hq, w.Hkv, w.d)
     return {"us_per_step": ms * 1e3, "tok_per_s": w.B / (ms * 1e-3), "host_read_bytes": host_read,
             "host_read_GBps": gbps, "frac_of_measured_read_peak": gbps / peak_read if peak_read else None,
-            "frac_of_pcie5_x16": gbps / PCIE5_X16_GBPS}
+            "frac_of_pcie5_x16": gbps / PCIE5_X16_GBPS,
+            "overlap_model": _overlap_model(1, past, host_read, flops, MFMA_PEAK_TFLOPS[w.dtype], ms, peak_read)}
 
 
 def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, variant="fused",
@@ -522,6 +541,9 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "past_len": int(past[0]), "new_tokens": 1,
                    "D": w.D, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "kv_cache": "pinned host memory"},
         "decode_tok_per_s": w.B / (ms * 1e-3),
+        "overlap_model": _overlap_model(
+            1, past, host_read, acc.attention_flops(past, 1, w.Hq, w.d) + acc.projection_flops(w.B, 1, w.D, w.Hq, w.Hkv, w.d),
+            MFMA_PEAK_TFLOPS[w.dtype], ms, peak["read"]),
         "roofline": {"bound": "host_link", "kernel": "decode_kernel (+combine) per attn_decode call",
                      "achieved": achieved, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                      "frac": achieved / PCIE5_X16_GBPS,

@@ -64,3 +64,13 @@ def _simulate_two_stage(n, comp, xfer):
 @pytest.mark.parametrize("n,comp,xfer", [(1, 120, 100), (7, 120, 100), (9, 80, 100), (5, 50, 50)])
 def test_pipeline_model_matches_event_simulation(n, comp, xfer):
     assert acc.pipeline_cycles(n, comp, xfer) == pytest.approx(_simulate_two_stage(n, comp, xfer))
+
+
+def test_overlap_model_limits():
+    # link-bound stream: the whole transfer plus one tile's compute
+    assert acc.overlap_model_seconds(100, 1e9, 1e6, 1e10, 1e12) == pytest.approx(0.1 + 1e-6 / 100)
+    # compute-bound stream: one tile's transfer plus the whole compute
+    assert acc.overlap_model_seconds(50, 1e6, 1e12, 1e10, 1e12) == pytest.approx(1e-4 / 50 + 1.0)
+    # one tile: no overlap at all
+    assert acc.overlap_model_seconds(1, 1e9, 1e12, 1e10, 1e12) == pytest.approx(0.1 + 1.0)
+    assert acc.overlap_model_seconds(0, 1e9, 1e12, 1e10, 1e12) == 0.0

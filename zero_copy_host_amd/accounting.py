@@ -54,3 +54,17 @@ def pipeline_cycles(n_tiles: int, compute: float, transfer: float) -> float:
     if n_tiles <= 0:
         return 0.0
     return transfer + (n_tiles - 1) * max(compute, transfer) + compute
+
+
+def overlap_model_seconds(n_tiles: int, host_bytes: float, flops: float, link_bytes_per_s: float,
+                          compute_flops_per_s: float) -> float:
+    """Expected time of one step under the two-stage pipeline model of the "DirectKV Guide"
+    (warp-level pipelining): the step's host bytes and flops are spread evenly over the
+    `n_tiles` key tiles of one stream, a tile's transfer runs at the link rate and its compute
+    at the compute rate, and the stream pays the first transfer, n - 1 overlapped tiles and the
+    last compute."""
+    if n_tiles <= 0:
+        return 0.0
+    transfer = host_bytes / n_tiles / link_bytes_per_s
+    compute = flops / n_tiles / compute_flops_per_s
+    return pipeline_cycles(n_tiles, compute, transfer)

@@ -41,8 +41,8 @@ namespace dkv {
 #ifndef DKV_ATTN_WAVES
 #define DKV_ATTN_WAVES 8   // waves per workgroup, 32 query rows each
 #endif
-#ifndef DKV_ATTN_MINWG
-#define DKV_ATTN_MINWG 1   // workgroups per CU the register allocation must allow
+#ifndef DKV_ATTN_MINWAVES
+#define DKV_ATTN_MINWAVES 2   // waves per SIMD the register allocation must allow (d = 128)
 #endif
 #ifndef DKV_ATTN_KPAD
 #define DKV_ATTN_KPAD 8    // elements of padding per K tile row (16-bit types)
@@ -54,7 +54,9 @@ namespace dkv {
 
 template <typename T, int DH>
 struct AttnCfg {
-  static constexpr int KT = sizeof(T) == 2 ? DKV_ATTN_KT : 64;   // keys per LDS tile
+  // keys per LDS tile; fp32 at d = 128 takes 32-key tiles, which keeps its scores, probabilities
+  // and tile loads within the register budget of two waves per SIMD
+  static constexpr int KT = sizeof(T) == 2 ? DKV_ATTN_KT : (DH == 128 ? 32 : 64);
   static constexpr int WAVES = DKV_ATTN_WAVES;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = 32 * WAVES;        // query rows per workgroup
@@ -80,7 +82,10 @@ constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max pas
 // PAGED: the host cache is a page pool addressed through the block table; the page ids of
 // the launch's host keys are staged in LDS before the sweep.
 template <typename T, int DH, int G, bool PAGED>
-__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kernel(const AttnArgs a) {
+// The second bound is the minimum number of waves per SIMD; 16-bit types at d = 64 fit two
+// workgroups per CU (four waves per SIMD, at most 128 VGPRs a lane).
+__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
+void attn_kernel(const AttnArgs a) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
   constexpr int KT = C::KT, VEC = C::VEC, LDK = C::LDK, LDV = C::LDV, LOADS = C::LOADS, DB = C::DB;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
       __syncthreads();
     }
     // element offset of host key j (row start) within the K or V pool
-    auto hrow = [&](int j) -> size_t {
+    auto hrow = [&](int j) __attribute__((always_inline)) -> size_t {
       if constexpr (PAGED)
         return (((size_t)s_pages[j / kPageTokens - pg0] * a.Hkv + g) * kPageTokens + j % kPageTokens) * DH;
       else
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
     // for the data anyway: a masked load into pre-zeroed registers would make the wave wait
     // for its loads right after issuing them.
     uint4 rk[2][LOADS], rv[2][LOADS];
-    auto gk = [&](int set, int j0) {
+    auto gk = [&](int set, int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int j = min(j0 + krow[i], key_hi - 1);
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
         rk[set][i] = *reinterpret_cast<const uint4*>(ks + e);
       }
     };
-    auto gv = [&](int set, int j0) {
+    auto gv = [&](int set, int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int j = min(j0 + krow[i], key_hi - 1);
@@ -232,14 +237,14 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
         rv[set][i] = *reinterpret_cast<const uint4*>(vs + e);
       }
     };
-    auto sk = [&](int buf, int set, int j0) {
+    auto sk = [&](int buf, int set, int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int kr = krow[i], kc = off[i] - kr * DH;
         *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = j0 + kr < key_hi ? rk[set][i] : make_uint4(0, 0, 0, 0);
       }
     };
-    auto sv = [&](int buf, int set, int j0) {
+    auto sv = [&](int buf, int set, int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int kr = krow[i], kc = off[i] - kr * DH;
@@ -253,13 +258,13 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
         }
       }
     };
-    auto gload = [&](int set, int j0) { gk(set, j0); gv(set, j0); };
-    auto sstore = [&](int buf, int set, int j0) { sk(buf, set, j0); sv(buf, set, j0); };
+    auto gload = [&](int set, int j0) __attribute__((always_inline)) { gk(set, j0); gv(set, j0); };
+    auto sstore = [&](int buf, int set, int j0) __attribute__((always_inline)) { sk(buf, set, j0); sv(buf, set, j0); };
 
     // ---- the three parts of a key tile (KT keys) against this wave's 32 query rows
     typedef f32x16 Scores[KT / 32];                      // Sᵀ: KT/32 blocks of 32 keys x 32 queries
     typedef typename MF::frag Probs[KT / 32][32 / KSTEP];  // Pᵀ in MFMA operand form
-    auto qk = [&](const T* tK, Scores& sc) {
+    auto qk = [&](const T* tK, Scores& sc) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
       }
     };
     // mask, tile maximum and the lazy raise of the reference maximum (rescaling o and l)
-    auto rebase = [&](const int j0, Scores& sc) {
+    auto rebase = [&](const int j0, Scores& sc) __attribute__((always_inline)) {
       // mask only where some row of this workgroup cannot see some key of the tile
       if ((j0 + KT > key_hi) || (j0 + KT > key_all)) {
 #pragma unroll
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
       }
     };
     // Pᵀ = exp2(Sᵀ·scale - m) in operand form, and the row sums into l
-    auto probs = [&](const Scores& sc, Probs& pb) {
+    auto probs = [&](const Scores& sc, Probs& pb) __attribute__((always_inline)) {
       const float mref = (m_run == -INFINITY) ? 0.f : m_run;
       float ps = 0.f;
 #pragma unroll
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
     };
     // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in accumulator
     // register stp*KPL + e of that half, i.e. element e of pb[kb][stp]
-    auto pv = [&](const T* tV, const Probs& pb) {
+    auto pv = [&](const T* tV, const Probs& pb) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb) {
 #pragma unroll
@@ -360,32 +365,39 @@ __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWG) void attn_kern
     };
 
     const int n = (key_hi - key_lo + KT - 1) / KT;     // key tiles in this launch
+    auto tj = [&](const int i) __attribute__((always_inline)) { return key_lo + i * KT; };   // tile i's first key
     Probs pb;
     // tile t computes from LDS buffer t % 2; register set 0 carries tiles 1, 3, 5, ... and set 1
     // tiles 2, 4, 6, ... (loaded two tiles ahead, stored to LDS one tile ahead)
     Scores sc;
-    auto tile = [&](const int j0, const int buf) {
+    auto tile = [&](const int j0, const int buf) __attribute__((always_inline)) {
       qk(sK[buf], sc);
       rebase(j0, sc);
       probs(sc, pb);
       pv(sV[buf], pb);
     };
-    gload(0, key_lo);
-    sstore(0, 0, key_lo);
-    if (n > 1) gload(0, key_lo + KT);
-    if (n > 2) gload(1, key_lo + 2 * KT);
+    // Loads are issued unconditionally, also for tiles past the end (their rows are clamped
+    // to the last key, which is already on chip): with a fixed issue order the wait before
+    // each LDS store counts only the loads of its own register set, not the newer ones.
+    gload(0, tj(0));
+    sstore(0, 0, tj(0));
+    gload(0, tj(1));
+    gload(1, tj(2));
     __syncthreads();
-    for (int t = 0; t < n; t += 2) {
-      tile(key_lo + t * KT, 0);
-      if (t + 1 < n) sstore(1, 0, key_lo + (t + 1) * KT);
-      if (t + 3 < n) gload(0, key_lo + (t + 3) * KT);
+    // whole pairs of tiles, then the odd tile: no exit mid-body, which keeps the load
+    // waits exact (each LDS store waits for its own register set only)
+    auto half = [&](const int i, const int buf, const int set) __attribute__((always_inline)) {
+      tile(tj(i), buf);
+      if (i + 1 < n) sstore(1 - buf, set, tj(i + 1));
+      gload(set, tj(i + 3));
       __syncthreads();
-      if (t + 1 >= n) break;
-      tile(key_lo + (t + 1) * KT, 1);
-      if (t + 2 < n) sstore(0, 1, key_lo + (t + 2) * KT);
-      if (t + 4 < n) gload(1, key_lo + (t + 4) * KT);
-      __syncthreads();
+    };
+    int i = 0;
+    for (; i + 1 < n; i += 2) {
+      half(i, 0, 0);
+      half(i + 1, 1, 1);
     }
+    if (i < n) half(i, 0, 0);
   }
 
   if (a.last) {
