@@ -65,24 +65,40 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
   const T* __restrict__ W = reinterpret_cast<const T*>(a.w[seg]);
   const int D = a.D;
 
-  uint4 rx[LOADS], rw[LOADS];
-  auto gload = [&](int k0) {
+  // Operand loads of reduction step kt into register set `set`. Every load is issued: rows
+  // past M or past the segment read the last valid row instead (their products land in
+  // outputs the epilogue never stores) and steps past the last read the last step, so each
+  // LDS store waits only for its own register set, two steps after the loads were issued.
+  const int nk = D / BK;
+  const int mlast = a.M - 1, nlast = nseg - 1;
+  // (two named register sets chosen by a branch, never an array indexed by the set, which
+  // the compiler would place in scratch memory once it merges the calls of both sets)
+  uint4 rx0[LOADS], rw0[LOADS], rx1[LOADS], rw1[LOADS];
+  auto gload = [&](const int set, const int kt) __attribute__((always_inline)) {
+    const int k0 = min(kt, nk - 1) * BK;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * 256;
       const int r = c / CPR, kc = (c % CPR) * VEC;
-      const int m = m0 + r, n = n0 + r;
-      rx[j] = (m < a.M) ? *reinterpret_cast<const uint4*>(X + (size_t)m * D + k0 + kc) : make_uint4(0, 0, 0, 0);
-      rw[j] = (n < nseg) ? *reinterpret_cast<const uint4*>(W + (size_t)n * D + k0 + kc) : make_uint4(0, 0, 0, 0);
+      const int m = min(m0 + r, mlast), n = min(n0 + r, nlast);
+      const uint4 vx = *reinterpret_cast<const uint4*>(X + (size_t)m * D + k0 + kc);
+      const uint4 vw = *reinterpret_cast<const uint4*>(W + (size_t)n * D + k0 + kc);
+      if (set == 0) {
+        rx0[j] = vx;
+        rw0[j] = vw;
+      } else {
+        rx1[j] = vx;
+        rw1[j] = vw;
+      }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const int buf, const int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int c = tid + j * 256;
       const int r = c / CPR, kc = (c % CPR) * VEC;
-      *reinterpret_cast<uint4*>(sX + buf * C::TILE + r * LDK + kc) = rx[j];
-      *reinterpret_cast<uint4*>(sW + buf * C::TILE + r * LDK + kc) = rw[j];
+      *reinterpret_cast<uint4*>(sX + buf * C::TILE + r * LDK + kc) = set == 0 ? rx0[j] : rx1[j];
+      *reinterpret_cast<uint4*>(sW + buf * C::TILE + r * LDK + kc) = set == 0 ? rw0[j] : rw1[j];
     }
   };
 
@@ -94,13 +110,9 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = D / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  // step kt computes from LDS buffer kt % 2; register set 0 carries steps 1, 3, 5, ... and set
+  // 1 steps 2, 4, 6, ... (loaded two steps ahead, stored to LDS one step ahead)
+  auto step = [&](const int kt, const int buf, const int set) __attribute__((always_inline)) {
     const T* tX = sX + buf * C::TILE;
     const T* tW = sW + buf * C::TILE;
 #pragma unroll
@@ -119,9 +131,21 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + 1 < nk) sstore(buf ^ 1, set);
+    gload(set, kt + 3);
     __syncthreads();
+  };
+  gload(0, 0);
+  sstore(0, 0);
+  gload(0, 1);
+  gload(1, 2);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {   // whole pairs of steps, no exit mid-body
+    step(kt, 0, 0);
+    step(kt + 1, 1, 1);
   }
+  if (kt < nk) step(kt, 0, 0);
 
   // ---- epilogue: round to T into an LDS tile, then write whole rows
   T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
