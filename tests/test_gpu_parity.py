@@ -68,6 +68,32 @@ def test_append_exact_bitwise_with_canaries(dtype, d):
             assert np.array_equal(arr_g[b, :, L + T:].view(np.uint8), arr_b[b, :, L + T:].view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [192, 320])
+def test_append_exact_odd_reduction_steps(dtype, D):
+    """D = 192 and 320 give the projection 3 and 5 reduction steps of 64: the loop's odd
+    last step, and operand loads issued past the last step, against exact-arithmetic inputs
+    (bitwise), with the rows around the appended ones untouched."""
+    case = _case(15, 2, 45, [3, 100], D, 4, 2, 64, dtype, exact=True)
+    g = GpuLayer(case, canary=True)
+    try:
+        before_k = g.cache.k.copy()
+        g.append(case["x"], case["past_len"])
+        kg, vg = g.cache.k.copy(), g.cache.v.copy()
+    finally:
+        g.free()
+    import oracle
+    B, T, Hkv, d = case["B"], case["T"], case["Hkv"], case["d"]
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    oracle.append(kc, oracle.project(case["x"], case["wk"]).reshape(B, T, Hkv, d), case["past_len"], dtype)
+    oracle.append(vc, oracle.project(case["x"], case["wv"]).reshape(B, T, Hkv, d), case["past_len"], dtype)
+    for b in range(B):
+        L = int(case["past_len"][b])
+        assert np.array_equal(kg[b, :, L:L + T], synth.to_storage(kc[b, :, L:L + T], dtype))
+        assert np.array_equal(vg[b, :, L:L + T], synth.to_storage(vc[b, :, L:L + T], dtype))
+        assert np.array_equal(kg[b, :, L + T:].view(np.uint8), before_k[b, :, L + T:].view(np.uint8))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_append_random_values(dtype):
     case = _case(12, 2, 300, [17, 250], 512, 8, 2, 128, dtype)
@@ -144,6 +170,8 @@ PREFILL_CASES = [
     (1, 130, [70], 256, 8, 4, 128, "f32"),
     (3, 150, [900, 0, 2500], 256, 16, 8, 64, "f16"),  # 24 pairs: three groups of 8
     (3, 100, [500, 0, 2200], 256, 8, 4, 64, "bf16"),  # 12 pairs: one launch group, 2 pairs per XCD
+    (1, 70, [33], 192, 4, 2, 64, "bf16"),            # 3 projection reduction steps (odd tail)
+    (2, 20, [0, 45], 320, 8, 8, 128, "f16"),         # 5 reduction steps; one key tile for b = 0
 ]
 
 
