@@ -51,7 +51,8 @@ typedef enum {
   DKV_OK = 0,
   DKV_ERR_INVALID_ARG = -1, /* null pointer, size <= 0, misalignment, Hq % Hkv != 0, D unsupported */
   DKV_ERR_CAPACITY = -2,    /* past_len[b] < 0 or past_len[b] + T > capacity */
-  DKV_ERR_UNSUPPORTED = -3, /* no kernel instance for this dtype / head_dim / group size */
+  DKV_ERR_UNSUPPORTED = -3, /* no kernel instance for this dtype / head_dim / group size, or a
+                               call with batch * n_kv_heads * T * head_dim >= 2^31 new K elements */
   DKV_ERR_HOST_ALLOC = -4,  /* pinned host allocation failed */
   DKV_ERR_HIP = -5,         /* a HIP runtime call failed */
   DKV_ERR_WORKSPACE = -6    /* ws is null or smaller than attn_workspace_bytes() */

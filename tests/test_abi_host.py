@@ -107,6 +107,11 @@ def test_call_validation_statuses(dkv):
     # unsupported head_dim / dtype in a descriptor
     assert L.kv_append(ctypes.byref(_fake_cache(dkv, d=96)), x, w, w, lp, 2, 1, 256, None) == -3
     assert L.kv_append(ctypes.byref(_fake_cache(dkv, dtype=5)), x, w, w, lp, 2, 1, 256, None) == -3
+    # more new K elements in one call than the kernels' 32-bit row indexing allows
+    big = _fake_cache(dkv, B=2, Hkv=8, d=128, cap=1 << 30)
+    bl, blp = _lens([0, 0])
+    assert L.kv_append(ctypes.byref(big), x, w, w, blp, 2, 1 << 20, 256, None) == -3
+    assert "2^31" in _err(dkv)
     # hostlink
     assert L.dkv_hostlink_stream(None, 1024, 0, 4, None) == -1
     assert L.dkv_hostlink_stream(0x1000, 1000, 0, 4, None) == -1
@@ -158,6 +163,17 @@ def _fake_paged(dkv, n_pages=8, Hkv=2, d=128, dtype=2):
 def _tab(rows):
     t = np.ascontiguousarray(np.array(rows, dtype=np.int32))
     return t, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), t.shape[1]
+
+
+def test_paged_alloc_validation(dkv):
+    L, pc = dkv.lib(), dkv.dkv_paged_cache()
+    assert L.kv_paged_alloc_host(None, 4, 2, 128, 2) == -1
+    assert L.kv_paged_alloc_host(ctypes.byref(pc), 0, 2, 128, 2) == -1
+    assert L.kv_paged_alloc_host(ctypes.byref(pc), 4, 2, 96, 2) == -3
+    # a pool whose byte count overflows is refused before any allocation
+    assert L.kv_paged_alloc_host(ctypes.byref(pc), 2**31 - 1, 2**31 - 1, 128, 0) == -1
+    assert "overflows" in _err(dkv)
+    assert pc.k is None and pc.reserved == 0
 
 
 def test_paged_table_validation(dkv):

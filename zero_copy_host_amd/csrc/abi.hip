@@ -75,6 +75,10 @@ int check_call(const dkv_cache* c, int32_t batch, int32_t T, int32_t D, const in
     if ((int64_t)past_len[b] + T > c->capacity)
       return fail(DKV_ERR_CAPACITY, "past_len[%d]=%d + T=%d exceeds capacity %d", b, past_len[b], T, c->capacity);
   }
+  // the kernels index the new rows of a call (and their 16-byte pieces) with 32-bit integers
+  if ((int64_t)batch * c->n_kv_heads * T * c->head_dim >= ((int64_t)1 << 31))
+    return fail(DKV_ERR_UNSUPPORTED, "batch*n_kv_heads*T*head_dim = %lld new K elements per call (limit 2^31)",
+                (long long)batch * c->n_kv_heads * T * c->head_dim);
   return DKV_OK;
 }
 
@@ -690,6 +694,8 @@ int kv_paged_alloc_host(dkv_paged_cache* out, int32_t n_pages, int32_t n_kv_head
   if (dtype < DKV_F32 || dtype > DKV_BF16) return fail(DKV_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (head_dim != 64 && head_dim != 128) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
   const size_t bytes = (size_t)n_pages * n_kv_heads * kPageTokens * head_dim * elem_size(dtype);
+  if (bytes / elem_size(dtype) / head_dim / kPageTokens / n_kv_heads != (size_t)n_pages)
+    return fail(DKV_ERR_INVALID_ARG, "page pool size overflows");
   void *k = nullptr, *v = nullptr;
   const unsigned flags = hipHostMallocMapped | hipHostMallocCoherent;
   hipError_t e = hipHostMalloc(&k, bytes, flags);
