@@ -211,7 +211,6 @@ ProjArgs make_proj(const dkv_cache* c, const void* x, const void* wq, const void
   a.n_seg[0] = wq ? n_q_heads * c->head_dim : 0;
   a.n_seg[1] = c->n_kv_heads * c->head_dim;
   a.n_seg[2] = c->n_kv_heads * c->head_dim;
-  for (int s = 0; s < 3; ++s) a.tiles_seg[s] = (a.n_seg[s] + 127) / 128;
   a.M = batch * T;
   a.D = D;
   a.T = T;

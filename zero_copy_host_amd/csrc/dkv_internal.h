@@ -121,7 +121,7 @@ struct ProjArgs {
   const void* x;            // [M = B*T, D]
   const void* w[3];         // segment weights [n_seg, D]; Q, K, V
   int32_t n_seg[3];         // output features per segment (0 = segment absent)
-  int32_t tiles_seg[3];     // 128-wide column tiles per segment
+  int32_t tiles_seg[3];     // column tiles per segment (set by the launcher)
   int32_t M, D, T, B, d, Hkv, cap;
   void* q_out;              // [M, n_seg[0]] device (segment 0)
   void* kc;                 // host cache K (segment 1), rows [past_len[b] + t]

@@ -9,44 +9,57 @@
 // back across the host link; in a fused prefill the host copy is then written by the first
 // attention launch, whose link traffic is otherwise all in the read direction.
 //
-// gfx950 mapping: 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, each
-// wave 2x2 blocks of the 32x32 MFMA; K steps of 64 through a double-buffered LDS tile
-// (X and W both stored k-contiguous, padded by 16 bytes per row against bank conflicts).
-// The reduction depth per stage (64) needs D % 64 == 0, which the ABI checks.
-// The epilogue is staged through LDS so every output row leaves as full 16-byte-per-lane
-// contiguous writes (whole host cache lines for K and V).
+// gfx950 mapping: 2x2 waves of 256 threads per workgroup; for 16-bit types each wave owns
+// 64 rows x 128 columns of Y (2x4 blocks of the 32x32x16 MFMA, accumulators in AGPRs), a
+// 128x256 workgroup tile, with reduction steps of 32 through a double-buffered LDS tile (X and
+// W both stored k-contiguous, padded by 16 bytes per row against bank conflicts). Per 16-deep
+// reduction slice a wave reads 2 + 4 operand fragments for 8 MFMAs (0.75 KB of LDS per MFMA;
+// a 64x64 wave tile needs 1 KB, which is the whole LDS bandwidth at the MFMA rate). fp32 keeps
+// 64x64 wave tiles with steps of 64. The reduction depth needs D % 64 == 0, which the ABI
+// checks. The epilogue is staged through LDS so every output row leaves as full 16-byte-per-
+// lane contiguous writes (whole host cache lines for K and V).
 #include "dkv_internal.h"
 
 namespace dkv {
 
 #ifndef DKV_PROJ_BK
-#define DKV_PROJ_BK 64   // reduction depth per LDS stage (build-time tunable)
+#define DKV_PROJ_BK 32   // reduction depth per LDS stage, 16-bit types (build-time tunable)
+#endif
+#ifndef DKV_PROJ_NB
+#define DKV_PROJ_NB 4    // 32-column MFMA blocks per wave, 16-bit types (build-time tunable)
 #endif
 
 template <typename T>
 struct ProjCfg {
-  static constexpr int BM = 128, BN = 128, BK = DKV_PROJ_BK;
   static constexpr int EB = sizeof(T);
+  static constexpr int MB = 2;                               // 32-row MFMA blocks per wave
+  static constexpr int NB = EB == 2 ? DKV_PROJ_NB : 2;       // 32-column MFMA blocks per wave
+  static constexpr int BK = EB == 2 ? DKV_PROJ_BK : 64;
+  static constexpr int BM = 2 * 32 * MB, BN = 2 * 32 * NB;   // 2x2 waves
   static constexpr int VEC = 16 / EB;            // elements per 16-byte chunk
   static constexpr int LDK = BK + VEC;           // padded row length in LDS (elements)
   static constexpr int CPR = BK / VEC;           // 16-byte chunks per tile row
-  static constexpr int LOADS = BM * CPR / 256;   // chunks per thread per operand tile
+  static constexpr int LOADS_X = BM * CPR / 256; // chunks per thread per X tile
+  static constexpr int LOADS_W = BN * CPR / 256; // chunks per thread per W tile
   static constexpr int LDO = BN + VEC;           // padded output staging row
-  static constexpr int TILE = BM * LDK;          // elements of one operand tile buffer
-  static constexpr int IN_BYTES = 4 * TILE * EB; // X and W, double buffered
+  static constexpr int TILE_X = BM * LDK, TILE_W = BN * LDK;   // elements of one buffer
+  static constexpr int IN_BYTES = 2 * (TILE_X + TILE_W) * EB;  // X and W, double buffered
   static constexpr int OUT_BYTES = BM * LDO * EB;
   static constexpr int SMEM = IN_BYTES > OUT_BYTES ? IN_BYTES : OUT_BYTES;
+  static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0 && 64 % BK == 0, "tile load mapping");
 };
 
+// 16-bit types: two workgroups per CU (at least two waves per SIMD, 256 registers a lane)
 template <typename T>
-__global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void proj_kernel(const ProjArgs a) {
   using C = ProjCfg<T>;
   using MF = Mfma<T>;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, LDK = C::LDK, CPR = C::CPR;
-  constexpr int LOADS = C::LOADS, KPL = MF::KPL, KSTEP = MF::KSTEP;
+  constexpr int MB = C::MB, NB = C::NB, LOADS_X = C::LOADS_X, LOADS_W = C::LOADS_W;
+  constexpr int KPL = MF::KPL, KSTEP = MF::KSTEP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
   T* sX = reinterpret_cast<T*>(smem);            // [2][BM][LDK]
-  T* sW = sX + 2 * C::TILE;                      // [2][BN][LDK]
+  T* sW = sX + 2 * C::TILE_X;                    // [2][BN][LDK]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -73,63 +86,68 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
   const int mlast = a.M - 1, nlast = nseg - 1;
   // (two named register sets chosen by a branch, never an array indexed by the set, which
   // the compiler would place in scratch memory once it merges the calls of both sets)
-  uint4 rx0[LOADS], rw0[LOADS], rx1[LOADS], rw1[LOADS];
+  uint4 rx0[LOADS_X], rw0[LOADS_W], rx1[LOADS_X], rw1[LOADS_W];
   auto gload = [&](const int set, const int kt) __attribute__((always_inline)) {
     const int k0 = min(kt, nk - 1) * BK;
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
+    for (int j = 0; j < LOADS_X; ++j) {
       const int c = tid + j * 256;
       const int r = c / CPR, kc = (c % CPR) * VEC;
-      const int m = min(m0 + r, mlast), n = min(n0 + r, nlast);
-      const uint4 vx = *reinterpret_cast<const uint4*>(X + (size_t)m * D + k0 + kc);
-      const uint4 vw = *reinterpret_cast<const uint4*>(W + (size_t)n * D + k0 + kc);
-      if (set == 0) {
-        rx0[j] = vx;
-        rw0[j] = vw;
-      } else {
-        rx1[j] = vx;
-        rw1[j] = vw;
-      }
+      const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)min(m0 + r, mlast) * D + k0 + kc);
+      if (set == 0) rx0[j] = v;
+      else rx1[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < LOADS_W; ++j) {
+      const int c = tid + j * 256;
+      const int r = c / CPR, kc = (c % CPR) * VEC;
+      const uint4 v = *reinterpret_cast<const uint4*>(W + (size_t)min(n0 + r, nlast) * D + k0 + kc);
+      if (set == 0) rw0[j] = v;
+      else rw1[j] = v;
     }
   };
   auto sstore = [&](const int buf, const int set) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
+    for (int j = 0; j < LOADS_X; ++j) {
       const int c = tid + j * 256;
       const int r = c / CPR, kc = (c % CPR) * VEC;
-      *reinterpret_cast<uint4*>(sX + buf * C::TILE + r * LDK + kc) = set == 0 ? rx0[j] : rx1[j];
-      *reinterpret_cast<uint4*>(sW + buf * C::TILE + r * LDK + kc) = set == 0 ? rw0[j] : rw1[j];
+      *reinterpret_cast<uint4*>(sX + buf * C::TILE_X + r * LDK + kc) = set == 0 ? rx0[j] : rx1[j];
+    }
+#pragma unroll
+    for (int j = 0; j < LOADS_W; ++j) {
+      const int c = tid + j * 256;
+      const int r = c / CPR, kc = (c % CPR) * VEC;
+      *reinterpret_cast<uint4*>(sW + buf * C::TILE_W + r * LDK + kc) = set == 0 ? rw0[j] : rw1[j];
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // step kt computes from LDS buffer kt % 2; register set 0 carries steps 1, 3, 5, ... and set
   // 1 steps 2, 4, 6, ... (loaded two steps ahead, stored to LDS one step ahead)
   auto step = [&](const int kt, const int buf, const int set) __attribute__((always_inline)) {
-    const T* tX = sX + buf * C::TILE;
-    const T* tW = sW + buf * C::TILE;
+    const T* tX = sX + buf * C::TILE_X;
+    const T* tW = sW + buf * C::TILE_W;
 #pragma unroll
     for (int ks = 0; ks < BK / KSTEP; ++ks) {
-      typename MF::frag fa[2], fb[2];
+      typename MF::frag fa[MB], fb[NB];
       const int kk = ks * KSTEP + (lane >> 5) * KPL;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const typename MF::frag*>(tX + r * LDK + kk);
-        const int cidx = wn * 64 + i * 32 + (lane & 31);
-        fb[i] = *reinterpret_cast<const typename MF::frag*>(tW + cidx * LDK + kk);
-      }
+      for (int i = 0; i < MB; ++i)
+        fa[i] = *reinterpret_cast<const typename MF::frag*>(tX + (wm * 32 * MB + i * 32 + (lane & 31)) * LDK + kk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < NB; ++j)
+        fb[j] = *reinterpret_cast<const typename MF::frag*>(tW + (wn * 32 * NB + j * 32 + (lane & 31)) * LDK + kk);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
     }
     if (kt + 1 < nk) sstore(buf ^ 1, set);
     gload(set, kt + 3);
@@ -150,13 +168,13 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
   // ---- epilogue: round to T into an LDS tile, then write whole rows
   T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + i * 32 + acc_row(v, lane);
-        const int cc = wn * 64 + j * 32 + (lane & 31);
+        const int r = wm * 32 * MB + i * 32 + acc_row(v, lane);
+        const int cc = wn * 32 * NB + j * 32 + (lane & 31);
         sO[r * C::LDO + cc] = Elem<T>::from_float(acc[i][j][v]);
       }
   __syncthreads();
@@ -184,8 +202,11 @@ __global__ __launch_bounds__(256) void proj_kernel(const ProjArgs a) {
 }
 
 template <typename T>
-static hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
-  const int mt = (a.M + ProjCfg<T>::BM - 1) / ProjCfg<T>::BM;
+static hipError_t launch_proj(const ProjArgs& args, hipStream_t s) {
+  constexpr int BM = ProjCfg<T>::BM, BN = ProjCfg<T>::BN;
+  ProjArgs a = args;
+  for (int g = 0; g < 3; ++g) a.tiles_seg[g] = (a.n_seg[g] + BN - 1) / BN;
+  const int mt = (a.M + BM - 1) / BM;
   const int nt = a.tiles_seg[0] + a.tiles_seg[1] + a.tiles_seg[2];
   hipLaunchKernelGGL(proj_kernel<T>, dim3(mt, nt), dim3(256), 0, s, a);
   return hipGetLastError();
