@@ -241,12 +241,16 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
         # one untimed call first (it writes the same row the first timed step rewrites)
         dkv.attn_decode(cache, xs[0], dev["wq"], dev["wk"], dev["wv"], past + w.T, w.Hq, outd, wsd)
         torch.cuda.synchronize()
+        # a single decode step is timed as the mean of 20 runs of that step (same lengths, so
+        # each run rewrites the same row); longer runs advance the lengths step by step
+        reps = 20 if decode_steps == 1 else 1
         with EventTimer() as t:
-            for s_ in range(decode_steps):
-                dkv.attn_decode(cache, xs[s_], dev["wq"], dev["wk"], dev["wv"], past + w.T + s_, w.Hq, outd, wsd)
-        ms = t.ms / decode_steps
+            for _ in range(reps):
+                for s_ in range(decode_steps):
+                    dkv.attn_decode(cache, xs[s_], dev["wq"], dev["wk"], dev["wv"], past + w.T + s_, w.Hq, outd, wsd)
+        ms = t.ms / (decode_steps * reps)
         mid = past + w.T + decode_steps // 2
-        res["decode"] = {"steps": decode_steps, "past_len_first": int(past[0] + w.T),
+        res["decode"] = {"steps": decode_steps, "timed_runs": decode_steps * reps, "past_len_first": int(past[0] + w.T),
                          **_decode_stats(w, mid, ms, peak_read)}
     cache.free()
     return res
