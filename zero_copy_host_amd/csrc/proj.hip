@@ -28,11 +28,14 @@ namespace dkv {
 #ifndef DKV_PROJ_NB
 #define DKV_PROJ_NB 4    // 32-column MFMA blocks per wave, 16-bit types (build-time tunable)
 #endif
+#ifndef DKV_PROJ_MB
+#define DKV_PROJ_MB 2    // 32-row MFMA blocks per wave, 16-bit types (build-time tunable)
+#endif
 
 template <typename T>
 struct ProjCfg {
   static constexpr int EB = sizeof(T);
-  static constexpr int MB = 2;                               // 32-row MFMA blocks per wave
+  static constexpr int MB = EB == 2 ? DKV_PROJ_MB : 2;       // 32-row MFMA blocks per wave
   static constexpr int NB = EB == 2 ? DKV_PROJ_NB : 2;       // 32-column MFMA blocks per wave
   static constexpr int BK = EB == 2 ? DKV_PROJ_BK : 64;
   static constexpr int BM = 2 * 32 * MB, BN = 2 * 32 * NB;   // 2x2 waves
@@ -49,9 +52,11 @@ struct ProjCfg {
   static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0 && 64 % BK == 0, "tile load mapping");
 };
 
-// 16-bit types: two workgroups per CU (at least two waves per SIMD, 256 registers a lane)
+// 16-bit types with the default tiles: two workgroups per CU (at least two waves per SIMD, 256
+// registers a lane)
 template <typename T>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void proj_kernel(const ProjArgs a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && DKV_PROJ_MB * DKV_PROJ_NB <= 8) ? 2 : 1)
+void proj_kernel(const ProjArgs a) {
   using C = ProjCfg<T>;
   using MF = Mfma<T>;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC, LDK = C::LDK, CPR = C::CPR;
