@@ -534,7 +534,7 @@ def main():
     host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)         # every past row, K and V, once
     host_write = acc.host_write_bytes(w.B, 1, w.Hkv, w.d, e)     # the new row
     achieved = host_read / (ms * 1e-3) / 1e9
-    traffic, host_meas = profile_traffic(src_hash("decode.hip"))
+    traffic, host_meas = profile_traffic(src_hash("decode.hip", "dkv_internal.h"))
     result = {
         "metric": "prefill tok/s & decode step us per layer; host-link GB/s vs measured peak",
         "value": ms * 1e3,
