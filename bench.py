@@ -464,8 +464,8 @@ def main():
                          "device-to-device copy)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the layer's host-KV path runs on a single MI355X and this "
-              f"build has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        print(f"bench.py measures one GPU: the host-KV layer path runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
     import torch
