@@ -138,10 +138,21 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
  *                        them back over the link;
  *   DKV_PREFILL_STAGED   the past rows are first copied (DMA) into a device staging copy of
  *                        the cache held in the workspace (attn_workspace_bytes phase 2), the
- *                        fused kernels run on that copy, and the new rows are copied back.
+ *                        fused kernels run on that copy, and the new rows are copied back;
+ *   DKV_PREFILL_PERSIST  the fused path as one persistent launch per group of 8 (sequence,
+ *                        kv head) pairs ([N] Key Idea (3), warp-level pipelining: a producer
+ *                        streams the next key super-chunk over the link while the current one
+ *                        is computed). Currently DISABLED: every call returns UNSUPPORTED, since
+ *                        its launch did not complete on the GPU and the cause is not found.
  * Errors: as attn_prefill, plus INVALID_ARG for an unknown variant.
  */
-enum { DKV_PREFILL_FUSED = 0, DKV_PREFILL_NAIVE = 1, DKV_PREFILL_SEPARATE = 2, DKV_PREFILL_STAGED = 3 };
+enum {
+  DKV_PREFILL_FUSED = 0,
+  DKV_PREFILL_NAIVE = 1,
+  DKV_PREFILL_SEPARATE = 2,
+  DKV_PREFILL_STAGED = 3,
+  DKV_PREFILL_PERSIST = 4
+};
 int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, const void* wk,
                          const void* wv, const int32_t* past_len, int32_t batch, int32_t T,
                          int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes,

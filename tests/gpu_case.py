@@ -59,7 +59,7 @@ class GpuLayer:
         self.wk = to_dev(c["wk"].T, dt)
         self.wv = to_dev(c["wv"].T, dt)
 
-    def prefill(self, x, past_len):
+    def prefill(self, x, past_len, variant=None):
         import torch
         c = self.c
         B, T, D = x.shape
@@ -67,7 +67,11 @@ class GpuLayer:
         out = torch.empty((B, T, c["Hq"] * c["d"]), dtype=torch_dtype(c["dtype"]), device="cuda")
         nb = self.dkv.workspace_bytes("prefill", self.cache, B, T, c["Hq"])
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
-        self.dkv.attn_prefill(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws)
+        if variant is None:
+            self.dkv.attn_prefill(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws)
+        else:
+            self.dkv.attn_prefill_variant(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws,
+                                          variant)
         torch.cuda.synchronize()
         return from_dev(out).reshape(B, T, c["Hq"], c["d"])
 

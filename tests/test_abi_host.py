@@ -95,7 +95,7 @@ def test_call_validation_statuses(dkv):
     bad.reserved = 0
     assert L.attn_decode(ctypes.byref(bad), x, w, w, w, lp, 2, 256, 4, out, ws, 1 << 30, None) == -1
     # unknown prefill / decode variant
-    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, 1 << 30, None, 4) == -1
+    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 2, 8, 256, 4, out, ws, 1 << 30, None, 5) == -1
     assert L.attn_decode_variant(ctypes.byref(c), x, w, w, w, lp, 2, 256, 4, out, ws, 1 << 30, None, 2) == -1
     # the staging baselines check their larger workspace before any copy: what the zero-copy
     # call needs is too small for them
@@ -135,9 +135,11 @@ def test_workspace_sizes(dkv):
     ws = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
     e = 2
     # queries + new K + new V + fp32 running state: per 32 query rows, 64 lanes x
-    # (d/32 * 16 accumulators + m + l)
+    # (d/32 * 16 accumulators + m + l); then the persistent launches' counters: 8 queue heads,
+    # 8 x 128 query tiles (256 rows each) and an error word
     want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
-    assert want <= ws <= want + 4 * 256
+    want += (8 + 8 * 128 + 1) * 4
+    assert want <= ws <= want + 5 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
     assert 0 < wsd < (1 << 24)
     # staging baselines: a device copy of the whole cache (K and V) on top
@@ -231,3 +233,12 @@ def test_paged_workspace_sizes(dkv):
             >= table_bytes + L.attn_workspace_bytes(1, ctypes.byref(cc), 2, 1, 32, lp))
     assert L.attn_paged_workspace_bytes(1, None, 2, 1, 32, 64) == 0
     assert L.attn_paged_workspace_bytes(1, ctypes.byref(c), 2, 1, 32, 0) == 0
+
+
+def test_disabled_persistent_prefill_is_refused_before_any_launch(dkv):
+    L = dkv.lib()
+    c = _fake_cache(dkv, B=1, Hkv=8, d=128, cap=4096)
+    lens, lp = _lens([1000])
+    x = w = out = ws = 0x10000
+    assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 1, 64, 256, 32, out, ws, 1 << 30, None, 4) == -3
+    assert "disabled" in _err(dkv)

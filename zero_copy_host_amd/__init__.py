@@ -25,7 +25,7 @@ EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes",
            "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
            "dkv_rmsnorm", "dkv_linear", "dkv_swiglu", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
 PAGE_TOKENS = 16
-PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2, "staged": 3}
+PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2, "staged": 3, "persistent": 4}
 DECODE_VARIANTS = {"zerocopy": 0, "staged": 1}
 
 

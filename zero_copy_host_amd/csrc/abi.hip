@@ -147,7 +147,7 @@ size_t decode_ws_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads, boo
 
 // ---- prefill workspace layout
 struct PrefillWs {
-  size_t q, k_new, v_new, state, total;
+  size_t q, k_new, v_new, state, sync, total;
 };
 
 PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
@@ -158,7 +158,10 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   w.k_new = w.q + round_up((size_t)batch * T * n_q_heads * d * e, 256);
   w.v_new = w.k_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
   w.state = w.v_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
-  w.total = w.state + round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
+  w.sync = w.state + round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
+  // persistent launches: 8 queue heads, 8 x q_tiles completion counters, an error word
+  const size_t q_tiles = ((size_t)T * std::max(1, G) + attn_rows_per_tile() - 1) / attn_rows_per_tile();
+  w.total = w.sync + round_up((8 + 8 * q_tiles + 1) * sizeof(int32_t), 256);
   return w;
 }
 
@@ -353,6 +356,33 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which
   // halves the launches every query tile makes and the running-state traffic they cost.
   const int group = aa.xcd_group && P % 8 == 0 ? 8 : P;
+  // (the persistent launch picks its queue by XCC id: it assumes one device of 8 XCDs of 32 CUs,
+  // the unpartitioned MI355X; on anything else the fused path runs)
+  if (variant == DKV_PREFILL_PERSIST && !paged && group == 8 && cu_count() == 256) {
+    // one persistent launch per group: each XCD holds the super-chunk it computes and the one
+    // its producer item brings in, so a super-chunk is half the per-launch size
+    attn_fn fpz = find_attn_persist(c->dtype, c->head_dim, G);
+    if (!fpz) return fail(DKV_ERR_UNSUPPORTED, "no persistent instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+    int32_t* sync = reinterpret_cast<int32_t*>(w + lay.sync);
+    const int n_sync = 8 + 8 * aa.q_tiles + 1;
+    aa.queue = sync;
+    aa.done = sync + 8;
+    aa.error = sync + 8 + 8 * aa.q_tiles;
+    aa.pre_slot = std::min(std::max(1, cu_count() / 8), aa.q_tiles);
+    for (int pair0 = 0; pair0 < P; pair0 += 8) {
+      int max_keys = 0;
+      for (int b = pair0 / c->n_kv_heads; b <= (pair0 + 7) / c->n_kv_heads; ++b)
+        max_keys = std::max(max_keys, past_len[b] + T);
+      aa.pair0 = pair0;
+      aa.pairs = 8;
+      aa.sk = superchunk_keys(c, 8, true);   // the quarter-L2 budget: two super-chunks resident
+      aa.max_keys = max_keys;
+      aa.n_sc = (max_keys + aa.sk - 1) / aa.sk;
+      if ((e = launch_zero_ints(sync, n_sync, s)) != hipSuccess) return hip_fail(e, "counter reset");
+      if ((e = fpz(aa, s)) != hipSuccess) return hip_fail(e, "attention launch");
+    }
+    return DKV_OK;
+  }
   for (int pair0 = 0; pair0 < P; pair0 += group) {
     aa.pair0 = pair0;
     aa.pairs = group;
@@ -668,8 +698,12 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   int st = check_call(c, batch, T, D, past_len, {x, wq, wk, wv, out});
   if (st) return st;
   if ((st = check_heads(c, n_q_heads))) return st;
-  if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_STAGED)
+  if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_PERSIST)
     return fail(DKV_ERR_INVALID_ARG, "unknown prefill variant %d", variant);
+  // The persistent launch did not complete on the GPU (its run never returned, also with every
+  // wait bounded); the cause is not found, so the variant is refused until it is.
+  if (variant == DKV_PREFILL_PERSIST)
+    return fail(DKV_ERR_UNSUPPORTED, "DKV_PREFILL_PERSIST is disabled: its launch did not complete on the GPU");
   if (T == 0) return DKV_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (variant != DKV_PREFILL_STAGED)

@@ -79,13 +79,37 @@ struct AttnCfg {
 
 constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max past 2^8
 
+// One unit of prefill attention work: the query tile qt of (sequence, kv head) pair p against
+// the key super-chunk [kc0, kc1); `first` = no running state to read yet, `last` = finalise
+// the output after this super-chunk.
+struct AttnItem {
+  int p, qt, kc0, kc1, first, last;
+};
+
+// Storer role: the (pair, token) rows [r0, r1) of this step's new K/V go from their device copy
+// to the host cache, 16 bytes per thread per step.
+template <typename T, int DH, bool PAGED>
+__device__ inline void attn_store(const AttnArgs& a, const int r0, const int r1) {
+  using C = AttnCfg<T, DH>;
+  constexpr int CPR = DH / C::VEC;
+  for (int c = r0 * CPR + (int)threadIdx.x; c < r1 * CPR; c += C::THREADS) {
+    const int row = c / CPR, col = (c - row * CPR) * C::VEC;
+    const int pp = row / a.T, t = row - pp * a.T;
+    const int bb = pp / a.Hkv;
+    const size_t src = ((size_t)pp * a.T + t) * DH + col;
+    const size_t dst = host_row(PAGED ? a.table : nullptr, a.max_pages, bb, pp - bb * a.Hkv, a.Hkv, a.cap,
+                                a.past_len[bb] + t) * DH + col;
+    const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.k_new) + src);
+    const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.v_new) + src);
+    *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.kc)) + dst) = kv;
+    *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.vc)) + dst) = vv;
+  }
+}
+
 // PAGED: the host cache is a page pool addressed through the block table; the page ids of
-// the launch's host keys are staged in LDS before the sweep.
+// the item's host keys are staged in LDS before the sweep.
 template <typename T, int DH, int G, bool PAGED>
-// The second bound is the minimum number of waves per SIMD; 16-bit types at d = 64 fit two
-// workgroups per CU (four waves per SIMD, at most 128 VGPRs a lane).
-__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
-void attn_kernel(const AttnArgs a) {
+__device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& a, const AttnItem it) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
   constexpr int KT = C::KT, VEC = C::VEC, LDK = C::LDK, LDV = C::LDV, LOADS = C::LOADS, DB = C::DB;
@@ -97,55 +121,17 @@ void attn_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int half = lane >> 5, col = lane & 31;
-
-  const int P = a.pairs;                         // pairs served by this launch, from a.pair0
-  if (a.store_new) {
-    // storer role: this step's new K/V rows go from their device copy to the host cache.
-    // The host hands each storing launch a share of the (pair, token) rows, [store_lo,
-    // store_hi), split among the launches that hold no host rows (so the writes cannot evict
-    // a resident super-chunk from L2) in proportion to their attention work, so the writes
-    // drain under their compute. Every workgroup copies its part before any early exit.
-    const int per = (a.store_hi - a.store_lo + gridDim.x - 1) / gridDim.x;
-    const int r0 = a.store_lo + blockIdx.x * per, r1 = min(r0 + per, a.store_hi);
-    constexpr int CPR = DH / C::VEC;
-    for (int c = r0 * CPR + (int)threadIdx.x; c < r1 * CPR; c += C::THREADS) {
-      const int row = c / CPR, col = (c - row * CPR) * C::VEC;
-      const int pp = row / a.T, t = row - pp * a.T;
-      const int bb = pp / a.Hkv;
-      const size_t src = ((size_t)pp * a.T + t) * DH + col;
-      const size_t dst = host_row(PAGED ? a.table : nullptr, a.max_pages, bb, pp - bb * a.Hkv, a.Hkv, a.cap,
-                                  a.past_len[bb] + t) * DH + col;
-      const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.k_new) + src);
-      const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.v_new) + src);
-      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.kc)) + dst) = kv;
-      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.vc)) + dst) = vv;
-    }
-  }
-  // workgroup -> (sequence/kv-head pair p, query tile qt). With at least 8 pairs, pair p is
-  // served only by XCD p % 8 (workgroup i runs on XCD i % 8). Query tiles go out last row
-  // first: under the causal mask later rows see more keys, so the longest tiles start first.
-  int p, qt;
-  if (a.xcd_group) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int ppx = (P + 7) >> 3;
-    const int lp = (slot % ppx) * 8 + xcd;
-    qt = a.q_tiles - 1 - slot / ppx;
-    if (lp >= P) return;
-    p = a.pair0 + lp;
-  } else {
-    p = a.pair0 + blockIdx.x % P;
-    qt = a.q_tiles - 1 - blockIdx.x / P;
-  }
+  const int p = it.p, qt = it.qt;
   const int b = p / a.Hkv, g = p - b * a.Hkv;
   const int L = a.past_len[b];
   const int nrows = a.T * G;                     // query rows of this pair: row = t*G + hh
   const int row0 = qt * C::ROWS;
   if (row0 >= nrows) return;
   const int rlast = min(row0 + C::ROWS, nrows) - 1;
-  const int key_hi = min(a.kc1, L + rlast / G + 1);   // keys any row here may see, exclusive
-  const int key_lo = a.kc0;
+  const int key_hi = min(it.kc1, L + rlast / G + 1);  // keys any row here may see, exclusive
+  const int key_lo = it.kc0;
   const bool work = key_lo < key_hi;
-  if (!work && !a.last) return;                  // nothing visible and nothing to finalise
+  if (!work && !it.last) return;                 // nothing visible and nothing to finalise
   const int key_all = L + row0 / G + 1;          // keys below this are visible to every row
 
   const int r = row0 + wave * 32 + col;          // this lane's query row
@@ -163,7 +149,7 @@ void attn_kernel(const AttnArgs a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-  if (!a.first && wvalid) {
+  if (!it.first && wvalid) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -404,7 +390,7 @@ void attn_kernel(const AttnArgs a) {
     if (i < n) half(i, 0, 0);
   }
 
-  if (a.last) {
+  if (it.last) {
     if (!rvalid) return;
     const float inv = 1.f / l_run;
     T* orow = reinterpret_cast<T*>(a.out) + (((size_t)b * a.T + t) * a.Hq + g * G + hh) * DH;
@@ -420,6 +406,187 @@ void attn_kernel(const AttnArgs a) {
       for (int v = 0; v < 16; ++v) __builtin_nontemporal_store(o[db][v], st + (db * 16 + v) * 64 + lane);
     __builtin_nontemporal_store(m_run, st + DB * 16 * 64 + lane);
     __builtin_nontemporal_store(l_run, st + (DB * 16 + 1) * 64 + lane);
+  }
+}
+
+// One launch per key super-chunk [a.kc0, a.kc1) of the pairs [a.pair0, a.pair0 + a.pairs).
+// The second bound is the minimum number of waves per SIMD; 16-bit types at d = 64 fit two
+// workgroups per CU (four waves per SIMD, at most 128 VGPRs a lane).
+template <typename T, int DH, int G, bool PAGED>
+__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
+void attn_kernel(const AttnArgs a) {
+  const int P = a.pairs;
+  if (a.store_new) {
+    // storer role: this step's new K/V rows go from their device copy to the host cache.
+    // The host hands each storing launch a share of the (pair, token) rows, [store_lo,
+    // store_hi), split among the launches that hold no host rows (so the writes cannot evict
+    // a resident super-chunk from L2) in proportion to their attention work, so the writes
+    // drain under their compute. Every workgroup copies its part before any early exit.
+    const int per = (a.store_hi - a.store_lo + gridDim.x - 1) / gridDim.x;
+    const int r0 = a.store_lo + blockIdx.x * per, r1 = min(r0 + per, a.store_hi);
+    attn_store<T, DH, PAGED>(a, r0, r1);
+  }
+  // workgroup -> (sequence/kv-head pair p, query tile qt). With at least 8 pairs, pair p is
+  // served only by XCD p % 8 (workgroup i runs on XCD i % 8). Query tiles go out last row
+  // first: under the causal mask later rows see more keys, so the longest tiles start first.
+  int p, qt;
+  if (a.xcd_group) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int ppx = (P + 7) >> 3;
+    const int lp = (slot % ppx) * 8 + xcd;
+    qt = a.q_tiles - 1 - slot / ppx;
+    if (lp >= P) return;
+    p = a.pair0 + lp;
+  } else {
+    p = a.pair0 + blockIdx.x % P;
+    qt = a.q_tiles - 1 - blockIdx.x / P;
+  }
+  attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, a.kc1, a.first, a.last});
+}
+
+// ---------------------------------------------------------------- persistent prefill
+// One launch per group of 8 (sequence, kv head) pairs, pair pair0 + x on XCD x, with a work
+// queue per XCD: for each key super-chunk s, the items (s, query tile) in heaviest-first order,
+// and after the first round of them a producer item that reads the pair's host rows of
+// super-chunk s + 1 into that XCD's L2. L2 keeps host lines only within one kernel, so here the
+// next super-chunk arrives over the link while this one is computed from L2, instead of in a
+// link-bound first round of its own launch. The running state (o, m, l) of a query tile passes
+// from item (s, qt) to item (s + 1, qt) through device memory: the writer waits for its stores
+// and bumps a per-tile counter with an L2 atomic; the reader polls that counter with an L2
+// atomic as well (a device-scope load is served beyond this XCD's L2 and does not see it) in a
+// bounded wait (items are taken in order, so the item it waits for is held by a running
+// workgroup), then drops its CU's L1 before reading the state. Every workgroup picks its queue from the XCC id register,
+// so writer and reader always share one L2, whatever the placement of workgroups.
+
+// A wait gives up (and flags the error word) after 0.25 s of the 100 MHz real-time clock; a
+// correct run waits at most about one item (well under a millisecond).
+constexpr unsigned long long kWaitTicks = 25000000ull;
+
+// the host rows [j0, j1) of pair p (K and V) are read once and dropped: they stay in L2
+template <typename T, int DH>
+__device__ inline void attn_prefetch(const AttnArgs& a, const int p, const int j0, const int j1) {
+  constexpr int THREADS = AttnCfg<T, DH>::THREADS;
+  const size_t base = ((size_t)p * a.cap + j0) * DH;
+  const size_t n16 = (size_t)(j1 - j0) * DH * sizeof(T) / 16;
+  const uint4* k = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kc) + base);
+  const uint4* v = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.vc) + base);
+  unsigned acc = 0;
+  for (size_t i = threadIdx.x; i < n16; i += 4 * THREADS) {
+    uint4 t[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t e = min(i + (size_t)u * THREADS, n16 - 1);   // in bounds; repeats are L2 hits
+      t[u] = k[e];
+      t[4 + u] = v[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= t[u].x ^ t[u].w;
+  }
+  if (acc == 0x9E3779B9u && a.sk < 0) atomicOr(a.error, (int)acc);   // keeps the loads (never true)
+}
+
+template <typename T, int DH, int G>
+__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
+void attn_persist_kernel(const AttnArgs a) {
+  __shared__ int s_item;
+  const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID: this XCD
+  const int p = a.pair0 + x;
+  const int b = p / a.Hkv;
+  const int L = a.past_len[b];
+  const int Q = a.q_tiles, S = a.n_sc, per_sc = Q + 1;
+  int* const done = a.done + (size_t)x * Q;
+  // the new rows of this pair are written to the host by the items of the super-chunks that
+  // hold none of its host rows, a share each
+  const int s_store = min(S - 1, (L + a.sk - 1) / a.sk);
+  const long long n_store = (long long)(S - s_store) * Q;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(a.queue + x, 1);
+    __syncthreads();
+    const int item = s_item;
+    __syncthreads();
+    if (item >= S * per_sc) break;
+    const int s = item / per_sc, r = item - s * per_sc;
+    const int kc0 = s * a.sk, kc1 = min(kc0 + a.sk, a.max_keys);
+    if (r == a.pre_slot) {
+      const int n1 = min(kc1 + a.sk, L);
+      if (kc1 < n1) attn_prefetch<T, DH>(a, p, kc1, n1);
+      continue;
+    }
+    const int ci = r < a.pre_slot ? r : r - 1;
+    const int qt = Q - 1 - ci;
+    if (s > 0) {
+      if (threadIdx.x == 0) {
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        // a compare-and-swap that never swaps (the counters are never -1) reads the counter with
+        // an L2 atomic, like the one that publishes (an atomic add of 0 would become a load)
+        while (atomicCAS(done + qt, -1, -1) < s) {
+          __builtin_amdgcn_s_sleep(2);
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            atomicOr(a.error, 1);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      asm volatile("buffer_inv sc0" ::: "memory");   // this CU's L1 may hold an older state
+    }
+    if (s >= s_store) {
+      const long long k = (long long)(s - s_store) * Q + ci;
+      const int t0 = (int)(a.T * k / n_store), t1 = (int)(a.T * (k + 1) / n_store);
+      attn_store<T, DH, false>(a, p * a.T + t0, p * a.T + t1);
+    }
+    attn_item<T, DH, G, false>(a, AttnItem{p, qt, kc0, kc1, s == 0, s == S - 1});
+    // publish: this item's state stores have reached L2 before the counter moves
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(done + qt, 1);
+  }
+}
+
+__global__ void zero_ints_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+template <typename T, int DH, int G>
+static hipError_t launch_attn_persist(const AttnArgs& a, hipStream_t s) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int per_xcd = cus / 8 > 0 ? cus / 8 : 1;   // one workgroup per CU
+  hipLaunchKernelGGL((attn_persist_kernel<T, DH, G>), dim3(8 * per_xcd), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+static attn_fn pick_persist_g(int G) {
+  switch (G) {
+    case 1: return launch_attn_persist<T, DH, 1>;
+    case 2: return launch_attn_persist<T, DH, 2>;
+    case 4: return launch_attn_persist<T, DH, 4>;
+    case 8: return launch_attn_persist<T, DH, 8>;
+    default: return nullptr;
+  }
+}
+
+template <typename T>
+static attn_fn pick_persist_d(int d, int G) {
+  if (d == 64) return pick_persist_g<T, 64>(G);
+  if (d == 128) return pick_persist_g<T, 128>(G);
+  return nullptr;
+}
+
+attn_fn find_attn_persist(int dtype, int d, int G) {
+  switch (dtype) {
+    case 0: return pick_persist_d<float>(d, G);
+    case 1: return pick_persist_d<_Float16>(d, G);
+    case 2: return pick_persist_d<__bf16>(d, G);
+    default: return nullptr;
   }
 }
 

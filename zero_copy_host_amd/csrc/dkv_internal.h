@@ -178,6 +178,11 @@ struct AttnArgs {
   int32_t store_lo, store_hi;  // (pair, token) rows [store_lo, store_hi) this launch copies
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
+  // persistent prefill: one launch per group of 8 pairs, a work queue per XCD
+  int32_t* queue;           // [8] next item of each XCD's queue (zero at launch)
+  int32_t* done;            // [8][q_tiles] items finished per query tile (zero at launch)
+  int32_t* error;           // set to 1 if a wait gave up (never in a correct run)
+  int32_t sk, n_sc, max_keys, pre_slot;   // keys per super-chunk, super-chunks, key range, producer slot
   int32_t past_len[kMaxBatch];
 };
 
@@ -192,6 +197,8 @@ proj_fn find_proj(int dtype, int d);
 decode_fn find_decode(int dtype, int d, int G, bool paged);
 combine_fn find_combine(int dtype, int d);
 attn_fn find_attn(int dtype, int d, int G, bool paged);
+attn_fn find_attn_persist(int dtype, int d, int G);   // contiguous caches, groups of 8 pairs
+hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
 
 int decode_slots(int dtype, int d);  // key rows one decode WG consumes per step
 int attn_rows_per_tile();            // query rows (token x head) per prefill WG
