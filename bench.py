@@ -548,7 +548,7 @@ def main():
         "overlap_model": _overlap_model(
             1, past, host_read, acc.attention_flops(past, 1, w.Hq, w.d) + acc.projection_flops(w.B, 1, w.D, w.Hq, w.Hkv, w.d),
             MFMA_PEAK_TFLOPS[w.dtype], ms, peak["read"]),
-        "roofline": {"bound": "host_link", "kernel": "decode_kernel (+combine) per attn_decode call",
+        "roofline": {"bound": "host_link", "kernel": "decode_kernel (+ qproj_kernel, combine_kernel) per attn_decode call",
                      "achieved": achieved, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                      "frac": achieved / PCIE5_X16_GBPS,
                      "peak_note": "PCIe 5.0 x16 per direction; measured kernel read peak below",

@@ -160,10 +160,13 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
 
 /*
  * One decode step (T = 1) for every sequence ([N] Attention Fusion Engine, decode
- * strategy): the new token's q, k, v are projected inside the attention kernel, k and v
- * are stored to host row past_len[b], and the query attends to rows 0 .. past_len[b]
- * (ragged lengths allowed). Split-KV: each split streams its share of the host rows once
- * and writes one partial; a combine merges them. out: [batch, 1, Hq*d].
+ * strategy): the new token's k and v are projected inside the attention kernel and stored
+ * to host row past_len[b], and the query attends to rows 0 .. past_len[b] (ragged lengths
+ * allowed). Split-KV: each split streams its share of the host rows once and writes one
+ * partial; a combine merges them. out: [batch, 1, Hq*d]. q is projected once per step by a
+ * small pre-pass into the workspace when the splits would otherwise re-read more than
+ * 256 MiB of Wq between them, else inside the attention kernel; both give bitwise the same q
+ * (the environment variable DIRECTKV_DECODE_QPASS=0 or 1 forces one of them).
  */
 int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* wk,
                 const void* wv, const int32_t* past_len, int32_t batch, int32_t D,

@@ -158,6 +158,32 @@ def test_decode_parity(shape):
         compare_rows(vg[b, :, L], vc[b, :, L], dtype, av[b, :, 0], D, "new V row")
 
 
+@pytest.mark.parametrize("shape", [(2, [2000, 3001], 512, 16, 2, 128, "bf16"), (3, [0, 1, 700], 256, 4, 4, 64, "f32"),
+                                   (1, [9000], 1024, 32, 8, 128, "f16")],
+                         ids=lambda s: f"B{s[0]}-L{max(s[1])}-G{s[3]//s[4]}-{s[6]}")
+def test_decode_query_prepass_is_bitwise_the_in_kernel_projection(shape, monkeypatch):
+    """Queries projected once per step by the pre-pass and queries projected by each decode
+    workgroup follow one summation order: the outputs and appended rows are bitwise equal."""
+    B, past, D, Hq, Hkv, d, dtype = shape
+    case = _case(17, B, 1, past, D, Hq, Hkv, d, dtype)
+    outs, rows = [], []
+    for mode in ("1", "0"):
+        monkeypatch.setenv("DIRECTKV_DECODE_QPASS", mode)
+        g = GpuLayer(case)
+        try:
+            outs.append(g.decode(case["x"], case["past_len"]))
+            rows.append([(g.cache.k[b, :, L].copy(), g.cache.v[b, :, L].copy())
+                         for b, L in enumerate(case["past_len"])])
+        finally:
+            g.free()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    for (k1, v1), (k0, v0) in zip(rows[0], rows[1]):
+        assert np.array_equal(k1.view(np.uint8), k0.view(np.uint8))
+        assert np.array_equal(v1.view(np.uint8), v0.view(np.uint8))
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    compare(outs[0], oracle_step(case, case["x"], case["past_len"], kc, vc), dtype, f"decode {shape}")
+
+
 # ------------------------------------------------------------------ prefill
 
 PREFILL_CASES = [

@@ -137,12 +137,34 @@ void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, boo
   p.split_begin[batch] = p.n_splits;
 }
 
-size_t decode_ws_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads, bool paged) {
+// decode workspace: the split partials, then the projected queries [B][Hq*d] fp32
+size_t decode_part_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads, bool paged) {
   // sum_b ceil((L_b+1)/chunk) <= keys/chunk + batch <= target + batch; a capped paged chunk adds
   // at most batch * (capacity / kPagedDecodeChunk + 1)
   size_t splits = (size_t)decode_target_splits(c) + batch + 1;
   if (paged) splits += (size_t)batch * ((size_t)c->capacity / kPagedDecodeChunk + 1);
   return round_up(splits * n_q_heads * (c->head_dim + 2) * sizeof(float), 256);
+}
+
+size_t decode_ws_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads, bool paged) {
+  return decode_part_bytes(c, batch, n_q_heads, paged) +
+         round_up((size_t)batch * n_q_heads * c->head_dim * sizeof(float), 256);
+}
+
+// Queries are projected once per step by a pre-pass when the decode workgroups projecting their
+// own would read Wq again by more than kQpassMinBytes: every split beyond a sequence's first
+// re-reads its group's G*d rows of D weights, for each kv head (a 70B-shaped layer re-reads ~8 GiB
+// per step, mostly beyond L2). Below that the extra launch costs more than the reads.
+// DIRECTKV_DECODE_QPASS=0/1 forces either (both give bitwise the same queries).
+constexpr size_t kQpassMinBytes = 256ull << 20;
+
+bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, int32_t n_q_heads, int32_t D) {
+  if (const char* env = getenv("DIRECTKV_DECODE_QPASS")) {
+    if (env[0] == '0') return false;
+    if (env[0] == '1') return true;
+  }
+  const size_t wq_bytes = (size_t)n_q_heads * c->head_dim * D * elem_size(c->dtype);   // all kv heads' slices
+  return (size_t)(p.n_splits - batch) * wq_bytes > kQpassMinBytes;
 }
 
 // ---- prefill workspace layout
@@ -260,7 +282,9 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   const int G = n_q_heads / c->n_kv_heads;
   decode_fn fd = find_decode(c->dtype, c->head_dim, G, paged);
   combine_fn fc = find_combine(c->dtype, c->head_dim);
-  if (!fd || !fc) return fail(DKV_ERR_UNSUPPORTED, "no decode instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
+  qproj_fn fq = find_qproj(c->dtype, c->head_dim);
+  if (!fd || !fc || !fq)
+    return fail(DKV_ERR_UNSUPPORTED, "no decode instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
 
   DecodePlan p;
   plan_decode(c, past_len, batch, paged, p);
@@ -273,6 +297,9 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   a.kc = c->k;
   a.vc = c->v;
   a.part = reinterpret_cast<float*>(ws);
+  a.qf = decode_uses_qpass(c, p, batch, n_q_heads, D)
+             ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + decode_part_bytes(c, batch, n_q_heads, paged))
+             : nullptr;
   a.B = batch;
   a.D = D;
   a.Hq = n_q_heads;
@@ -294,7 +321,9 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   ca.n_splits = p.n_splits;
   for (int b = 0; b <= batch; ++b) ca.split_begin[b] = p.split_begin[b];
 
-  hipError_t e = fd(a, s);
+  hipError_t e;
+  if (a.qf && (e = fq(a, s)) != hipSuccess) return hip_fail(e, "query projection launch");
+  e = fd(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   e = fc(ca, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");

@@ -59,6 +59,62 @@ __device__ void project_rows(const float* __restrict__ sx, const T* __restrict__
   }
 }
 
+// log2(e)/sqrt(d): scores come out in the base-2 exponent domain
+__device__ inline float qproj_scale(int dh) { return 1.4426950408889634f * rsqrtf((float)dh); }
+
+// The queries of a decode step, every (sequence, query head), projected once:
+// qf[b][n] = qproj_scale(d) * sum_k x[b][k] * wq[n][k]. Each weight row streams from HBM once per
+// BB sequences. The sum over k runs in project_rows' order (lane-strided vectors of VEC, fma in
+// order, then the wave's xor tree), so these are bitwise the values a decode workgroup would
+// compute for itself.
+template <typename T, int DH, int R, int BB>
+__global__ __launch_bounds__(256) void qproj_kernel(const DecodeArgs a) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nrows = a.Hq * DH;
+  const int r0 = (blockIdx.x * 4 + wave) * R;
+  const int b0 = blockIdx.y * BB;
+  const int nb = min(BB, a.B - b0);
+  if (r0 >= nrows) return;
+  const T* __restrict__ w = reinterpret_cast<const T*>(a.wq);
+  const T* __restrict__ x = reinterpret_cast<const T*>(a.x) + (size_t)b0 * a.D;
+  float acc[R][BB];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int j = 0; j < BB; ++j) acc[i][j] = 0.f;
+  // several k steps of weight loads in flight per wave (the loop bound keeps every load in D)
+#pragma unroll 4
+  for (int k = lane * VEC; k < a.D; k += 64 * VEC) {
+    float f[R][VEC];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      // a row past the end reads row 0 (in bounds); its sums are never stored
+      const int row = r0 + i < nrows ? r0 + i : 0;
+      Elem<T>::unpack(*reinterpret_cast<const uint4*>(w + (size_t)row * a.D + k), f[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < BB; ++j) {
+      if (j < nb) {
+        float xs[VEC];
+        Elem<T>::unpack(*reinterpret_cast<const uint4*>(x + (size_t)j * a.D + k), xs);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[i][j] = fmaf(f[i][e], xs[e], acc[i][j]);
+      }
+    }
+  }
+  const float scale = qproj_scale(DH);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int j = 0; j < BB; ++j) {
+      const float v = wave_sum(acc[i][j]);
+      if (lane == 0 && j < nb && r0 + i < nrows) a.qf[(size_t)(b0 + j) * nrows + r0 + i] = v * scale;
+    }
+}
+
 template <typename T, int DH, int G>
 struct DecodeCfg {
   static constexpr int VEC = Elem<T>::VEC;
@@ -101,13 +157,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int i = tid; i < npg; i += blockDim.x) s_pages[i] = a.table[(size_t)b * a.max_pages + pg0 + i];
   }
 
-  // ---- projection of this token: q for heads g*G .. g*G+G-1 (and k, v if new)
-  const T* __restrict__ xrow = reinterpret_cast<const T*>(a.x) + (size_t)b * a.D;
-  for (int k = tid; k < a.D; k += blockDim.x) s_buf[k] = Elem<T>::to_float(xrow[k]);
+  // ---- projection of this token: q for heads g*G .. g*G+G-1 (and k, v if new). With several
+  // splits per sequence the queries come projected once per step (a.qf, qproj_kernel), so the
+  // Wq slice (G*d rows of D) is not read again by every split of the group.
+  if (!a.qf || has_new) {
+    const T* __restrict__ xrow = reinterpret_cast<const T*>(a.x) + (size_t)b * a.D;
+    for (int k = tid; k < a.D; k += blockDim.x) s_buf[k] = Elem<T>::to_float(xrow[k]);
+  }
   __syncthreads();
-  // log2(e)/sqrt(d): scores come out in the base-2 exponent domain
-  const float qscale = 1.4426950408889634f * rsqrtf((float)DH);
-  project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wq), a.D, g * G * DH, G * DH, s_q, qscale);
+  if (a.qf) {
+    const float* __restrict__ qsrc = a.qf + (size_t)b * a.Hq * DH + (size_t)g * G * DH;
+    for (int i = tid; i < G * DH; i += blockDim.x) s_q[i] = qsrc[i];
+  } else {
+    project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wq), a.D, g * G * DH, G * DH, s_q, qproj_scale(DH));
+  }
   if (has_new) {
     project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wk), a.D, g * DH, DH, s_kv, 1.f);
     project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wv), a.D, g * DH, DH, s_kv + DH, 1.f);
@@ -311,6 +374,17 @@ static hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+constexpr int kQprojRows = 1;    // weight rows per wave: many waves per SIMD hide the HBM latency
+constexpr int kQprojBatch = 8;   // sequences per workgroup (more go to further grid rows)
+
+template <typename T, int DH>
+static hipError_t launch_qproj(const DecodeArgs& a, hipStream_t s) {
+  const int rows_per_wg = 4 * kQprojRows;
+  const dim3 grid((a.Hq * DH + rows_per_wg - 1) / rows_per_wg, (a.B + kQprojBatch - 1) / kQprojBatch);
+  hipLaunchKernelGGL((qproj_kernel<T, DH, kQprojRows, kQprojBatch>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // ---- pre-instantiated kernel table (dtype x head_dim x group size x cache layout)
 template <typename T, int DH, bool PAGED>
 static decode_fn pick_g(int G) {
@@ -345,6 +419,16 @@ combine_fn find_combine(int dtype, int d) {
     case 0: return d == 64 ? launch_combine<float, 64> : launch_combine<float, 128>;
     case 1: return d == 64 ? launch_combine<_Float16, 64> : launch_combine<_Float16, 128>;
     case 2: return d == 64 ? launch_combine<__bf16, 64> : launch_combine<__bf16, 128>;
+    default: return nullptr;
+  }
+}
+
+qproj_fn find_qproj(int dtype, int d) {
+  if (d != 64 && d != 128) return nullptr;
+  switch (dtype) {
+    case 0: return d == 64 ? launch_qproj<float, 64> : launch_qproj<float, 128>;
+    case 1: return d == 64 ? launch_qproj<_Float16, 64> : launch_qproj<_Float16, 128>;
+    case 2: return d == 64 ? launch_qproj<__bf16, 64> : launch_qproj<__bf16, 128>;
     default: return nullptr;
   }
 }

@@ -142,6 +142,8 @@ struct DecodeArgs {
   void* kc;                 // host cache
   void* vc;
   float* part;              // [n_splits_total][Hq][d + 2]: o (unnormalised), m, l
+  float* qf;                // [B][Hq*d] queries projected once per step and pre-scaled by
+                            // log2(e)/sqrt(d), or null: each workgroup projects its own
   int32_t B, D, Hq, Hkv, cap, n_splits;
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
@@ -192,10 +194,12 @@ typedef hipError_t (*proj_fn)(const ProjArgs&, hipStream_t);
 typedef hipError_t (*decode_fn)(const DecodeArgs&, hipStream_t);
 typedef hipError_t (*combine_fn)(const CombineArgs&, hipStream_t);
 typedef hipError_t (*attn_fn)(const AttnArgs&, hipStream_t);
+typedef hipError_t (*qproj_fn)(const DecodeArgs&, hipStream_t);   // fills a.qf
 
 proj_fn find_proj(int dtype, int d);
 decode_fn find_decode(int dtype, int d, int G, bool paged);
 combine_fn find_combine(int dtype, int d);
+qproj_fn find_qproj(int dtype, int d);
 attn_fn find_attn(int dtype, int d, int G, bool paged);
 attn_fn find_attn_persist(int dtype, int d, int G);   // contiguous caches, groups of 8 pairs
 hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
