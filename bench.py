@@ -494,7 +494,9 @@ def main():
               flush=True)
         return
     if args.profile == "prefill":
-        print(json.dumps({"prefill": run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=args.steps,
+        # the 8B chunked prefill unless --workload names another prefill workload
+        name = args.workload if synth.workload(args.workload).T > 1 else "llama8b_prefill_T8192_on_L24576_bf16"
+        print(json.dumps({"prefill": run_prefill(dkv, name, steps=args.steps,
                                                  warmup=args.warmup, variant=args.variant)}), flush=True)
         return
     if args.profile:

@@ -215,6 +215,23 @@ def test_prefill_parity(shape):
         compare_rows(vg[b, :, L:L + T], vc[b, :, L:L + T], dtype, av[b], D, "new V rows")
 
 
+def test_prefill_long_launch_super_chunks_sampled_rows():
+    """257 query tiles of 256 rows for the one (sequence, kv head) pair: the planner takes the
+    smaller super-chunk it uses for launches with many rounds of query tiles (3072 keys at bf16,
+    d = 128), whose boundaries fall inside the past and inside the new keys. Sampled token rows
+    (every head) against the oracle, and every appended row."""
+    B, T, past, D, Hq, Hkv, d, dtype = 1, 8200, [2000], 256, 8, 1, 128, "bf16"
+    ts = np.array(sorted({0, 1, 1071, 1072, 3000, 4095, 4096, 7167, 7168, 8191, 8198, 8199}))
+    case = _case(19, B, T, past, D, Hq, Hkv, d, dtype)
+    out, ref, kg, vg, kc, vc = _run_prefill(case, t_index=ts, canary=True)
+    compare(out, ref, dtype, "long-launch prefill, sampled rows")
+    ak = absdot_rows(case["x"], case["wk"], Hkv, d)
+    av = absdot_rows(case["x"], case["wv"], Hkv, d)
+    L = past[0]
+    compare_rows(kg[0, :, L:L + T], kc[0, :, L:L + T], dtype, ak[0], D, "new K rows")
+    compare_rows(vg[0, :, L:L + T], vc[0, :, L:L + T], dtype, av[0], D, "new V rows")
+
+
 def test_tiny_layer_prefill_then_decode():
     """The tiny fp32 layer: causal prefill of 128 tokens into an empty cache, then one
     decode step reading the cache the prefill wrote."""

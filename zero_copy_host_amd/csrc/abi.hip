@@ -190,8 +190,15 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
 // keys per super-chunk: the host KV of every (sequence, kv head) pair an XCD serves
 // during one launch must fit about half of that XCD's 4 MB L2 (a quarter for a paged cache:
 // its super-chunk is scattered over the pool in 4 KB (page, head) blocks, which at half the
-// L2 conflict-miss and are fetched again, 1.28x the host bytes against 1.02x at a quarter)
-int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged) {
+// L2 conflict-miss and are fetched again, 1.28x the host bytes against 1.02x at a quarter).
+// With more than kLongLaunchTiles query tiles per pair a launch runs many rounds of query tiles,
+// whose running-state streams pass through L2 between the uses of the super-chunk: there it
+// takes three eighths of L2 (70B-shaped prefill, 512 tiles per pair: host reads 1.15x the
+// algorithmic bytes at a half, 1.02x at three eighths, 1.00x at a quarter, for 74.2, 76.0 and
+// 80.1 ms; the 8B-shaped prefill, 128 tiles per pair, reads 1.03x at a half).
+constexpr int kLongLaunchTiles = 256;
+
+int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged, int32_t q_tiles) {
   // a paged launch stages the page ids of its keys in LDS: at most kPagedSuperchunk keys
   const size_t limit = paged ? kPagedSuperchunk : 1 << 20;
   // tuning override (keys, multiple of 64)
@@ -201,7 +208,8 @@ int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged) {
   }
   const int per_xcd = std::max(1, (pairs + 7) / 8);
   const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);  // K and V
-  size_t keys = ((size_t)(paged ? 1 : 2) << 20) / ((size_t)per_xcd * row_bytes);
+  const size_t budget = paged ? (1u << 20) : q_tiles > kLongLaunchTiles ? (3u << 19) : (2u << 20);
+  size_t keys = budget / ((size_t)per_xcd * row_bytes);
   keys = std::max<size_t>(64, keys / 64 * 64);
   return (int)std::min<size_t>(keys, limit);
 }
@@ -404,7 +412,7 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
         max_keys = std::max(max_keys, past_len[b] + T);
       aa.pair0 = pair0;
       aa.pairs = 8;
-      aa.sk = superchunk_keys(c, 8, true);   // the quarter-L2 budget: two super-chunks resident
+      aa.sk = superchunk_keys(c, 8, true, aa.q_tiles);   // the quarter-L2 budget: two super-chunks resident
       aa.max_keys = max_keys;
       aa.n_sc = (max_keys + aa.sk - 1) / aa.sk;
       if ((e = launch_zero_ints(sync, n_sync, s)) != hipSuccess) return hip_fail(e, "counter reset");
@@ -426,7 +434,7 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
       max_past = std::max(max_past, past_len[b]);
     }
     // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
-    const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged);
+    const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged, aa.q_tiles);
     const int nsc = (max_keys + sk - 1) / sk;
     // The new rows' host copies are written by launches whose keys hold no host rows (no
     // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
