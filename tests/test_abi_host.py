@@ -118,6 +118,18 @@ def test_call_validation_statuses(dkv):
     assert L.dkv_hostlink_stream(0x1000, 1024, 2, 4, None) == -1
 
 
+def test_batch_limit(dkv):
+    """Lengths travel in kernel arguments: at most 256 sequences per call; more is UNSUPPORTED
+    before anything is enqueued."""
+    L = dkv.lib()
+    c = _fake_cache(dkv, B=257)
+    lens, lp = _lens([1] * 257)
+    assert L.attn_decode(ctypes.byref(c), 0x10000, 0x10000, 0x10000, 0x10000, lp, 257, 256, 2,
+                         0x10000, 0x10000, 1 << 30, None) == -3
+    assert "257" in _err(dkv)
+    assert L.kv_append(ctypes.byref(c), 0x10000, 0x10000, 0x10000, lp, 257, 1, 256, None) == -3
+
+
 def test_zero_new_tokens_is_a_no_op(dkv):
     L = dkv.lib()
     c = _fake_cache(dkv)

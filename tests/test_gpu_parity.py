@@ -184,6 +184,33 @@ def test_decode_query_prepass_is_bitwise_the_in_kernel_projection(shape, monkeyp
     compare(outs[0], oracle_step(case, case["x"], case["past_len"], kc, vc), dtype, f"decode {shape}")
 
 
+def test_decode_at_the_batch_limit(monkeypatch):
+    """256 sequences (the most one call takes) with ragged lengths from 0 up: one to three
+    splits each, the split table's last entries, and the query pre-pass's 32 grid rows of 8
+    sequences. Both query paths against the oracle, and bitwise against each other."""
+    B, D, Hq, Hkv, d, dtype = 256, 128, 8, 2, 64, "bf16"
+    past = [int(v) for v in synth.Draw(23).lengths(B, 0, 300)]
+    past[0], past[-1] = 0, 300
+    case = _case(23, B, 1, past, D, Hq, Hkv, d, dtype)
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    ref = oracle_step(case, case["x"], case["past_len"], kc, vc)
+    outs = []
+    for mode in ("1", "0"):
+        monkeypatch.setenv("DIRECTKV_DECODE_QPASS", mode)
+        g = GpuLayer(case)
+        try:
+            outs.append(g.decode(case["x"], case["past_len"]))
+            kg = g.cache_k()
+        finally:
+            g.free()
+        compare(outs[-1], ref, dtype, f"decode B=256 qpass={mode}")
+        ak = absdot_rows(case["x"], case["wk"], Hkv, d)
+        for b in (0, 1, 127, 255):
+            L = int(case["past_len"][b])
+            compare_rows(kg[b, :, L], kc[b, :, L], dtype, ak[b, :, 0], D, f"new K row of sequence {b}")
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 # ------------------------------------------------------------------ prefill
 
 PREFILL_CASES = [
