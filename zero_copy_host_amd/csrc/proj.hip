@@ -9,13 +9,14 @@
 // back across the host link; in a fused prefill the host copy is then written by the first
 // attention launch, whose link traffic is otherwise all in the read direction.
 //
-// gfx950 mapping: 2x2 waves of 256 threads per workgroup; for 16-bit types each wave owns
-// 64 rows x 128 columns of Y (2x4 blocks of the 32x32x16 MFMA, accumulators in AGPRs), a
-// 128x256 workgroup tile, with reduction steps of 32 through a double-buffered LDS tile (X and
-// W both stored k-contiguous, padded by 16 bytes per row against bank conflicts). Per 16-deep
+// gfx950 mapping: for 16-bit types 4x2 waves (512 threads) per workgroup, one workgroup per CU;
+// each wave owns 64 rows x 128 columns of Y (2x4 blocks of the 32x32x16 MFMA), a 256x256
+// workgroup tile, with reduction steps of 32 through a double-buffered LDS tile (X and W both
+// stored k-contiguous, padded by 16 bytes per row against bank conflicts). Per 16-deep
 // reduction slice a wave reads 2 + 4 operand fragments for 8 MFMAs (0.75 KB of LDS per MFMA;
-// a 64x64 wave tile needs 1 KB, which is the whole LDS bandwidth at the MFMA rate). fp32 keeps
-// 64x64 wave tiles with steps of 64. The reduction depth needs D % 64 == 0, which the ABI
+// a 64x64 wave tile needs 1 KB, which is the whole LDS bandwidth at the MFMA rate), and the CU
+// pulls 32 KB of operands from L2 per step against 48 KB for two 128x256 workgroups. fp32
+// keeps 2x2 waves of 64x64 tiles with steps of 64. The reduction depth needs D % 64 == 0, which the ABI
 // checks. The epilogue is staged through LDS so every output row leaves as full 16-byte-per-
 // lane contiguous writes (whole host cache lines for K and V).
 #include "dkv_internal.h"
@@ -31,6 +32,9 @@ namespace dkv {
 #ifndef DKV_PROJ_MB
 #define DKV_PROJ_MB 2    // 32-row MFMA blocks per wave, 16-bit types (build-time tunable)
 #endif
+#ifndef DKV_PROJ_WM
+#define DKV_PROJ_WM 4    // waves along M per workgroup, 16-bit types (build-time tunable; 2 columns of waves)
+#endif
 
 template <typename T>
 struct ProjCfg {
@@ -38,24 +42,29 @@ struct ProjCfg {
   static constexpr int MB = EB == 2 ? DKV_PROJ_MB : 2;       // 32-row MFMA blocks per wave
   static constexpr int NB = EB == 2 ? DKV_PROJ_NB : 2;       // 32-column MFMA blocks per wave
   static constexpr int BK = EB == 2 ? DKV_PROJ_BK : 64;
-  static constexpr int BM = 2 * 32 * MB, BN = 2 * 32 * NB;   // 2x2 waves
+  static constexpr int WM = EB == 2 ? DKV_PROJ_WM : 2, WN = 2;   // waves along M and N
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int BM = WM * 32 * MB, BN = WN * 32 * NB;
   static constexpr int VEC = 16 / EB;            // elements per 16-byte chunk
   static constexpr int LDK = BK + VEC;           // padded row length in LDS (elements)
   static constexpr int CPR = BK / VEC;           // 16-byte chunks per tile row
-  static constexpr int LOADS_X = BM * CPR / 256; // chunks per thread per X tile
-  static constexpr int LOADS_W = BN * CPR / 256; // chunks per thread per W tile
+  static constexpr int LOADS_X = BM * CPR / THREADS; // chunks per thread per X tile
+  static constexpr int LOADS_W = BN * CPR / THREADS; // chunks per thread per W tile
   static constexpr int LDO = BN + VEC;           // padded output staging row
   static constexpr int TILE_X = BM * LDK, TILE_W = BN * LDK;   // elements of one buffer
   static constexpr int IN_BYTES = 2 * (TILE_X + TILE_W) * EB;  // X and W, double buffered
   static constexpr int OUT_BYTES = BM * LDO * EB;
   static constexpr int SMEM = IN_BYTES > OUT_BYTES ? IN_BYTES : OUT_BYTES;
-  static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0 && 64 % BK == 0, "tile load mapping");
+  static_assert(BM * CPR % THREADS == 0 && BN * CPR % THREADS == 0 && 64 % BK == 0, "tile load mapping");
+  // waves per SIMD the register allocation must allow (256 registers a lane at two)
+  static constexpr int MIN_WAVES = (EB == 2 && DKV_PROJ_MB * DKV_PROJ_NB <= 8) ? 2 : 1;
 };
 
-// 16-bit types with the default tiles: two workgroups per CU (at least two waves per SIMD, 256
-// registers a lane)
+// 16-bit types with the default tiles: one 256x256 workgroup of 8 waves per CU, two waves per
+// SIMD (256 registers a lane). Against two 128x256 workgroups per CU it loads a third fewer
+// operand bytes per MFMA into the CU.
 template <typename T>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 && DKV_PROJ_MB * DKV_PROJ_NB <= 8) ? 2 : 1)
+__global__ __launch_bounds__(ProjCfg<T>::THREADS, ProjCfg<T>::MIN_WAVES)
 void proj_kernel(const ProjArgs a) {
   using C = ProjCfg<T>;
   using MF = Mfma<T>;
@@ -66,8 +75,9 @@ void proj_kernel(const ProjArgs a) {
   T* sX = reinterpret_cast<T*>(smem);            // [2][BM][LDK]
   T* sW = sX + 2 * C::TILE_X;                    // [2][BN][LDK]
 
+  constexpr int THREADS = C::THREADS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;          // WM x 2 waves
 
   // which segment and column tile this workgroup owns. The K and V tiles, whose epilogue
   // writes go over the host link, are dispatched first so that those posted writes drain
@@ -96,7 +106,7 @@ void proj_kernel(const ProjArgs a) {
     const int k0 = min(kt, nk - 1) * BK;
 #pragma unroll
     for (int j = 0; j < LOADS_X; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * THREADS;
       const int r = c / CPR, kc = (c % CPR) * VEC;
       const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)min(m0 + r, mlast) * D + k0 + kc);
       if (set == 0) rx0[j] = v;
@@ -104,7 +114,7 @@ void proj_kernel(const ProjArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < LOADS_W; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * THREADS;
       const int r = c / CPR, kc = (c % CPR) * VEC;
       const uint4 v = *reinterpret_cast<const uint4*>(W + (size_t)min(n0 + r, nlast) * D + k0 + kc);
       if (set == 0) rw0[j] = v;
@@ -114,13 +124,13 @@ void proj_kernel(const ProjArgs a) {
   auto sstore = [&](const int buf, const int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LOADS_X; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * THREADS;
       const int r = c / CPR, kc = (c % CPR) * VEC;
       *reinterpret_cast<uint4*>(sX + buf * C::TILE_X + r * LDK + kc) = set == 0 ? rx0[j] : rx1[j];
     }
 #pragma unroll
     for (int j = 0; j < LOADS_W; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * THREADS;
       const int r = c / CPR, kc = (c % CPR) * VEC;
       *reinterpret_cast<uint4*>(sW + buf * C::TILE_W + r * LDK + kc) = set == 0 ? rw0[j] : rw1[j];
     }
@@ -184,7 +194,7 @@ void proj_kernel(const ProjArgs a) {
       }
   __syncthreads();
   constexpr int CH = BN / VEC;                   // 16-byte chunks per output row
-  for (int c = tid; c < BM * CH; c += 256) {
+  for (int c = tid; c < BM * CH; c += THREADS) {
     const int r = c / CH, cc = (c % CH) * VEC;
     const int m = m0 + r, n = n0 + cc;
     if (m >= a.M || n >= nseg) continue;
@@ -213,7 +223,7 @@ static hipError_t launch_proj(const ProjArgs& args, hipStream_t s) {
   for (int g = 0; g < 3; ++g) a.tiles_seg[g] = (a.n_seg[g] + BN - 1) / BN;
   const int mt = (a.M + BM - 1) / BM;
   const int nt = a.tiles_seg[0] + a.tiles_seg[1] + a.tiles_seg[2];
-  hipLaunchKernelGGL(proj_kernel<T>, dim3(mt, nt), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(proj_kernel<T>, dim3(mt, nt), dim3(ProjCfg<T>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
