@@ -14,6 +14,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/directkv.h"
@@ -435,30 +436,46 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
     }
     // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
     const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged, aa.q_tiles);
-    const int nsc = (max_keys + sk - 1) / sk;
+    // Key ranges of the launches: super-chunks of sk keys while some sequence of the group
+    // still has host rows in them. The keys after that are this step's rows; when they come
+    // from their device copies they need no L2 budget and go in one launch, which saves each
+    // query tile a running-state round trip per extra launch and lets the short tiles of the
+    // causal triangle run beside the long ones. (The separate-kernels baseline reads them from
+    // the host cache, so they keep the super-chunk size there.)
+    std::vector<std::pair<int, int>> ranges;
+    int first_free = -1;
+    for (int k0 = 0; k0 < max_keys; k0 += sk) {
+      if (k0 >= max_past && first_free < 0) {
+        first_free = (int)ranges.size();
+        if (!separate) {
+          ranges.emplace_back(k0, max_keys);
+          break;
+        }
+      }
+      ranges.emplace_back(k0, std::min(k0 + sk, max_keys));
+    }
+    const int nl = (int)ranges.size();
     // The new rows' host copies are written by launches whose keys hold no host rows (no
-    // past KV of any sequence in their super-chunk), so the writes cannot evict a resident
+    // past KV of any sequence in their range), so the writes cannot evict a resident
     // super-chunk from L2; with no such launch, the last one writes them all. The rows are
     // split among those launches in proportion to their attention work.
-    int first_free = nsc - 1;
-    for (int i = 0; i < nsc; ++i)
-      if (i * sk >= max_past) { first_free = i; break; }
+    if (first_free < 0) first_free = nl - 1;
     auto launch_work = [&](int i) {
       long long wk_ = 0;
       for (int b = b0; b <= b1; ++b)
-        wk_ += npairs(b) * visible_keys(past_len[b], T, i * sk, std::min((i + 1) * sk, max_keys));
+        wk_ += npairs(b) * visible_keys(past_len[b], T, ranges[i].first, ranges[i].second);
       return wk_;
     };
     long long work_total = 0;
-    for (int i = first_free; i < nsc; ++i) work_total += launch_work(i);
+    for (int i = first_free; i < nl; ++i) work_total += launch_work(i);
     const long long new_rows = (long long)group * T;       // (pair, token) rows of this group
     const long long row0 = (long long)pair0 * T;
     long long work_before = 0;
-    for (int i = 0; i < nsc; ++i) {
-      aa.kc0 = i * sk;
-      aa.kc1 = std::min((i + 1) * sk, max_keys);
+    for (int i = 0; i < nl; ++i) {
+      aa.kc0 = ranges[i].first;
+      aa.kc1 = ranges[i].second;
       aa.first = i == 0;
-      aa.last = i == nsc - 1;
+      aa.last = i == nl - 1;
       aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
       if (aa.store_new) {
         const long long wl = launch_work(i);
@@ -466,8 +483,8 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
           aa.store_lo = (int)(row0 + new_rows * work_before / work_total);
           aa.store_hi = (int)(row0 + new_rows * (work_before + wl) / work_total);
         } else {
-          aa.store_lo = (int)(row0 + new_rows * (i - first_free) / (nsc - first_free));
-          aa.store_hi = (int)(row0 + new_rows * (i - first_free + 1) / (nsc - first_free));
+          aa.store_lo = (int)(row0 + new_rows * (i - first_free) / (nl - first_free));
+          aa.store_hi = (int)(row0 + new_rows * (i - first_free + 1) / (nl - first_free));
         }
         work_before += wl;
       }
