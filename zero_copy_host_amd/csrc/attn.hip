@@ -16,9 +16,9 @@
 // super-chunk through double-buffered LDS tiles (loads issued two tiles ahead), and carries
 // the per-row softmax state (o, m, l) in device memory from one super-chunk launch to the
 // next. Keys below past_len[b] come from the host cache; this step's new keys come from the
-// device copy the projection left, so they never cross the link a second time. Launches
-// whose keys hold no host rows also write this step's new rows to the host cache (the
-// storer role), a share each.
+// device copy the projection left, so they never cross the link a second time. The launch
+// (or launches) whose keys hold no host rows also writes this step's new rows to the host
+// cache (the storer role), a share each.
 //
 // MFMA layout: scores are computed transposed, Sᵀ = K·Qᵀ (32 keys x 32 queries per block),
 // so each lane owns one query column: row max / sum need one cross-half exchange, the
