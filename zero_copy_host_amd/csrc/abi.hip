@@ -436,23 +436,25 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
     }
     // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
     const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged, aa.q_tiles);
-    // Key ranges of the launches: super-chunks of sk keys while some sequence of the group
-    // still has host rows in them. The keys after that are this step's rows; when they come
-    // from their device copies they need no L2 budget and go in one launch, which saves each
-    // query tile a running-state round trip per extra launch and lets the short tiles of the
-    // causal triangle run beside the long ones. (The separate-kernels baseline reads them from
-    // the host cache, so they keep the super-chunk size there.)
+    // Key ranges of the launches: super-chunks of sk keys over the group's past keys, the last
+    // one ending at the longest past length. The keys after that are this step's rows; when
+    // they come from their device copies they need no L2 budget and go in one launch, which
+    // saves each query tile a running-state round trip per extra launch and lets the short
+    // tiles of the causal triangle run beside the long ones. (The separate-kernels baseline
+    // reads them from the host cache, so it keeps super-chunks over every key.)
     std::vector<std::pair<int, int>> ranges;
     int first_free = -1;
-    for (int k0 = 0; k0 < max_keys; k0 += sk) {
-      if (k0 >= max_past && first_free < 0) {
-        first_free = (int)ranges.size();
-        if (!separate) {
-          ranges.emplace_back(k0, max_keys);
-          break;
-        }
+    if (variant == DKV_PREFILL_NAIVE) {
+      ranges.emplace_back(0, max_keys);   // query-stationary: every key in one launch
+    } else if (separate) {
+      for (int k0 = 0; k0 < max_keys; k0 += sk) {
+        if (k0 >= max_past && first_free < 0) first_free = (int)ranges.size();
+        ranges.emplace_back(k0, std::min(k0 + sk, max_keys));
       }
-      ranges.emplace_back(k0, std::min(k0 + sk, max_keys));
+    } else {
+      for (int k0 = 0; k0 < max_past; k0 += sk) ranges.emplace_back(k0, std::min(k0 + sk, max_past));
+      first_free = (int)ranges.size();
+      ranges.emplace_back(max_past, max_keys);
     }
     const int nl = (int)ranges.size();
     // The new rows' host copies are written by launches whose keys hold no host rows (no
