@@ -452,7 +452,11 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
         ranges.emplace_back(k0, std::min(k0 + sk, max_keys));
       }
     } else {
-      for (int k0 = 0; k0 < max_past; k0 += sk) ranges.emplace_back(k0, std::min(k0 + sk, max_past));
+      // as many super-chunks as sk needs, of equal size (a multiple of 64 keys, at most sk), so
+      // that no launch sweeps a short remainder
+      const int n_host = (max_past + sk - 1) / sk;
+      const int skp = n_host > 0 ? std::min<int>(sk, (int)round_up((max_past + n_host - 1) / n_host, 64)) : sk;
+      for (int k0 = 0; k0 < max_past; k0 += skp) ranges.emplace_back(k0, std::min(k0 + skp, max_past));
       first_free = (int)ranges.size();
       ranges.emplace_back(max_past, max_keys);
     }
