@@ -225,6 +225,9 @@ PREFILL_CASES = [
     (3, 100, [500, 0, 2200], 256, 8, 4, 64, "bf16"),  # 12 pairs: one launch group, 2 pairs per XCD
     (1, 70, [33], 192, 4, 2, 64, "bf16"),            # 3 projection reduction steps (odd tail)
     (2, 20, [0, 45], 320, 8, 8, 128, "f16"),         # 5 reduction steps; one key tile for b = 0
+    (1, 1, [0], 256, 4, 4, 64, "f32"),               # one token on an empty cache: its own V
+    (3, 1, [1000, 0, 63], 256, 16, 2, 128, "bf16"),  # one token per sequence, ragged pasts
+    (2, 1, [64, 4096], 256, 32, 8, 128, "f16"),      # one token after a whole tile / super-chunk
 ]
 
 
