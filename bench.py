@@ -584,12 +584,16 @@ def main():
         log("70B prefill + 64 decode steps")
         big = run_prefill(dkv, "llama70b_prefill_T16384_on_L49152_b2_bf16", steps=2, warmup=1, peak_read=pr,
                           decode_steps=64)
+        log("70B prefill from an empty cache + 64 decode steps (the other reading of that case)")
+        big0 = run_prefill(dkv, "llama70b_prefill_T16384_empty_b2_bf16", steps=2, warmup=1, peak_read=pr,
+                           decode_steps=64)
         log("paged host cache: 8B decode and 8B chunked prefill")
         result["paged"] = run_paged(dkv, peak_read=pr)
         result["workloads"] = {"tiny_f32_prefill128_decode1": tiny,
                                "llama8b_prefill_T8192_on_L24576_bf16": result["prefill"],
                                "long_decode_b4_L96k_128k_f16": longd,
-                               "llama70b_prefill_T16384_on_L49152_b2_bf16": big}
+                               "llama70b_prefill_T16384_on_L49152_b2_bf16": big,
+                               "llama70b_prefill_T16384_empty_b2_bf16": big0}
     print(json.dumps(result), flush=True)
 
 

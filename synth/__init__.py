@@ -95,7 +95,7 @@ class Workload:
         return self.Hq // self.Hkv
 
 
-# The five workloads, in a fixed order; the seed of workload i is 1000 + i.
+# The workloads, in a fixed order; the seed of workload i is 1000 + i.
 # cap = rows per (sequence, kv head) in the host cache, rounded up to a multiple of 64.
 WORKLOADS = [
     Workload("tiny_f32_prefill128_decode1", "f32", D=256, Hq=4, Hkv=4, d=64,
@@ -108,6 +108,11 @@ WORKLOADS = [
              B=4, T=1, past=None, cap=131136, past_lo=98304, past_hi=131072, seed=1003),
     Workload("llama70b_prefill_T16384_on_L49152_b2_bf16", "bf16", D=8192, Hq=64, Hkv=8, d=128,
              B=2, T=16384, past=[49152] * 2, cap=65600, decode_steps=64, seed=1004),
+    # the other reading of the 70B-shaped case (a sensitivity row): the 65536 tokens are only
+    # the cache capacity, the 16384-token prefill starts from an empty cache and the 64 decode
+    # steps run at 16384 + s past tokens
+    Workload("llama70b_prefill_T16384_empty_b2_bf16", "bf16", D=8192, Hq=64, Hkv=8, d=128,
+             B=2, T=16384, past=[0] * 2, cap=16448, decode_steps=64, seed=1005),
 ]
 
 
