@@ -153,11 +153,11 @@ def test_workspace_sizes(dkv):
     want += (8 + 8 * 128 + 1) * 4
     assert want <= ws <= want + 5 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
-    # decode: fp32 partials (o, m, l) for at most 2 * 256 / Hkv + B + 1 splits, then the fp32
-    # queries [B][Hq*d] that the pre-pass projects once per step
+    # decode: fp32 partials (o, m, l) for at most 2 * (2 * 256 / Hkv) + B + 1 splits (the split
+    # target doubles for short chunks), then the fp32 queries [B][Hq*d] the pre-pass projects
     def up(n):
         return (n + 255) // 256 * 256
-    assert wsd == up((2 * 256 // 8 + 1 + 1) * 32 * (128 + 2) * 4) + up(1 * 32 * 128 * 4)
+    assert wsd == up((4 * 256 // 8 + 1 + 1) * 32 * (128 + 2) * 4) + up(1 * 32 * 128 * 4)
     # staging baselines: a device copy of the whole cache (K and V) on top
     staging = 2 * 1 * 8 * 32768 * 128 * e
     assert L.attn_workspace_bytes(2, ctypes.byref(c), 1, 8192, 32, lp) == staging + ws

@@ -112,18 +112,24 @@ struct DecodePlan {
   int split_begin[kMaxBatch + 1];
 };
 
+// Splits per kv head so that the whole grid is ~2 workgroups per CU, or ~4 when that would
+// leave each split fewer than kShortChunk keys: more, shorter host streams keep the link busier
+// there (70B-shaped decode at 16384 past tokens: 2.58 -> 2.51 ms per step), while at long
+// lengths they cost the extra partials (the same at 65536: 9.71 -> 9.75 ms; 8B-shaped at 32768:
+// 19.24 ms either way).
 constexpr int kDecodeWgPerCu = 2;
+constexpr int64_t kShortChunk = 1024;
 
 int decode_target_splits(const dkv_cache* c) {
-  // workgroups per kv head so that the whole grid is ~2 per CU
   return std::max(1, kDecodeWgPerCu * 256 / c->n_kv_heads);
 }
 
 void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, bool paged, DecodePlan& p) {
   int64_t keys = 0;
   for (int b = 0; b < batch; ++b) keys += past_len[b] + 1;
-  const int target = decode_target_splits(c);
+  int target = decode_target_splits(c);
   const int unit = decode_slots(c->dtype, c->head_dim);  // keys one loop iteration consumes
+  if ((keys + target - 1) / target < kShortChunk) target *= 2;
   int64_t chunk = (keys + target - 1) / target;
   chunk = std::max<int64_t>(chunk, 2 * unit);
   chunk = round_up(chunk, unit);
@@ -140,9 +146,9 @@ void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, boo
 
 // decode workspace: the split partials, then the projected queries [B][Hq*d] fp32
 size_t decode_part_bytes(const dkv_cache* c, int32_t batch, int32_t n_q_heads, bool paged) {
-  // sum_b ceil((L_b+1)/chunk) <= keys/chunk + batch <= target + batch; a capped paged chunk adds
-  // at most batch * (capacity / kPagedDecodeChunk + 1)
-  size_t splits = (size_t)decode_target_splits(c) + batch + 1;
+  // sum_b ceil((L_b+1)/chunk) <= keys/chunk + batch <= target + batch, target at most twice
+  // decode_target_splits; a capped paged chunk adds at most batch * (capacity / kPagedDecodeChunk + 1)
+  size_t splits = 2 * (size_t)decode_target_splits(c) + batch + 1;
   if (paged) splits += (size_t)batch * ((size_t)c->capacity / kPagedDecodeChunk + 1);
   return round_up(splits * n_q_heads * (c->head_dim + 2) * sizeof(float), 256);
 }
