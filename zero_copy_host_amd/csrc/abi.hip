@@ -630,11 +630,12 @@ Paging stage_table(const int32_t* table, int32_t batch, int32_t max_pages, void*
   return pg;
 }
 
-// common front of the paged calls: descriptor, table, workspace; on success `view` and `pg`
-// describe the call and the workspace past the table is returned in ws_rest/ws_rest_bytes
+// common front of the paged calls: descriptor, table, workspace; on success `view` describes
+// the call and the workspace past the table is returned in ws_rest/ws_rest_bytes (the caller
+// copies the table into the front of the workspace once its own checks pass)
 int paged_front(const dkv_paged_cache* pc, const int32_t* table, int32_t max_pages, const int32_t* past_len,
-                int32_t batch, int32_t T, void* ws, size_t ws_bytes, size_t need_rest, hipStream_t s,
-                dkv_cache& view, Paging& pg, void*& ws_rest, size_t& ws_rest_bytes) {
+                int32_t batch, int32_t T, void* ws, size_t ws_bytes, size_t need_rest,
+                dkv_cache& view, void*& ws_rest, size_t& ws_rest_bytes) {
   int st = check_paged(pc);
   if (st) return st;
   if ((st = check_table(pc, table, max_pages, past_len, batch, T))) return st;
@@ -644,7 +645,6 @@ int paged_front(const dkv_paged_cache* pc, const int32_t* table, int32_t max_pag
   view = paged_view(pc, batch, max_pages);
   ws_rest = reinterpret_cast<char*>(ws) + tb;
   ws_rest_bytes = ws_bytes - tb;
-  (void)s;
   return DKV_OK;
 }
 
@@ -848,7 +848,7 @@ int kv_paged_append(const dkv_paged_cache* c, const int32_t* block_table, int32_
   Paging pg;
   void* rest;
   size_t rest_bytes;
-  int st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, 0, s, view, pg, rest, rest_bytes);
+  int st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, 0, view, rest, rest_bytes);
   if (st) return st;
   if ((st = check_call(&view, batch, T, D, past_len, {x, wk, wv}))) return st;
   if (T == 0) return DKV_OK;
@@ -873,7 +873,7 @@ int attn_decode_paged(const dkv_paged_cache* c, const int32_t* block_table, int3
   const dkv_cache pre = paged_view(c, batch, max_pages);
   if (n_q_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "n_q_heads must be positive");
   const size_t need = decode_ws_bytes(&pre, batch, n_q_heads, true);
-  st = paged_front(c, block_table, max_pages, past_len, batch, 1, ws, ws_bytes, need, s, view, pg, rest, rest_bytes);
+  st = paged_front(c, block_table, max_pages, past_len, batch, 1, ws, ws_bytes, need, view, rest, rest_bytes);
   if (st) return st;
   if ((st = check_call(&view, batch, 1, D, past_len, {x, wq, wk, wv, out}))) return st;
   if ((st = check_heads(&view, n_q_heads))) return st;
@@ -900,7 +900,7 @@ int attn_prefill_paged(const dkv_paged_cache* c, const int32_t* block_table, int
   if (n_q_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "n_q_heads must be positive");
   const dkv_cache pre = paged_view(c, batch, max_pages);
   const size_t need = prefill_layout(&pre, batch, T, n_q_heads).total;
-  st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, need, s, view, pg, rest, rest_bytes);
+  st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, need, view, rest, rest_bytes);
   if (st) return st;
   if ((st = check_call(&view, batch, T, D, past_len, {x, wq, wk, wv, out}))) return st;
   if ((st = check_heads(&view, n_q_heads))) return st;
