@@ -563,10 +563,6 @@ def main():
                      "traffic": traffic, "host_read_bytes_measured": host_meas},
         "host_link": {"kernel_read_GBps": peak["read"], "kernel_write_GBps": peak["write"]},
     }
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host cores")
-        result["cpu_baseline"] = cpu_baseline_decode(w, s)
-    s["cache"].free()
     if not args.no_prefill:
         pr = peak["read"]
         log("other workloads: tiny fp32 layer")
@@ -594,6 +590,12 @@ def main():
                                "long_decode_b4_L96k_128k_f16": longd,
                                "llama70b_prefill_T16384_on_L49152_b2_bf16": big,
                                "llama70b_prefill_T16384_empty_b2_bf16": big0}
+    if not args.no_cpu_baseline:
+        # after every GPU measurement: the oracle's threads on all host cores would otherwise
+        # slow the kernel launches of the launch-bound workloads measured after it
+        log("timing the oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline_decode(w, s)
+    s["cache"].free()
     print(json.dumps(result), flush=True)
 
 
