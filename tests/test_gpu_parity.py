@@ -184,6 +184,28 @@ def test_decode_query_prepass_is_bitwise_the_in_kernel_projection(shape, monkeyp
     compare(outs[0], oracle_step(case, case["x"], case["past_len"], kc, vc), dtype, f"decode {shape}")
 
 
+@pytest.mark.parametrize("shape", [(1, [0], 256, 4, 4, 64, "f32"), (4, [0, 5, 100, 120], 256, 16, 4, 128, "bf16"),
+                                   (2, [63, 64], 512, 16, 2, 128, "f16")],
+                         ids=lambda s: f"B{s[0]}-L{max(s[1])}-G{s[3]//s[4]}-{s[6]}")
+def test_single_split_decode_writes_the_output_directly(shape, monkeypatch):
+    """With one split per sequence the decode kernel writes the output itself (no combine
+    launch): bitwise what the combine gives from the same partials, and within the tolerance of
+    the oracle."""
+    B, past, D, Hq, Hkv, d, dtype = shape
+    case = _case(29, B, 1, past, D, Hq, Hkv, d, dtype)
+    outs = []
+    for mode in ("0", "1"):
+        monkeypatch.setenv("DIRECTKV_DECODE_COMBINE", mode)
+        g = GpuLayer(case)
+        try:
+            outs.append(g.decode(case["x"], case["past_len"]))
+        finally:
+            g.free()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    compare(outs[0], oracle_step(case, case["x"], case["past_len"], kc, vc), dtype, f"decode {shape}")
+
+
 def test_decode_at_the_batch_limit(monkeypatch):
     """256 sequences (the most one call takes) with ragged lengths from 0 up: one to three
     splits each, the split table's last entries, and the query pre-pass's 32 grid rows of 8

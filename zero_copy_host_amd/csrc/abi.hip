@@ -312,6 +312,11 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   a.kc = c->k;
   a.vc = c->v;
   a.part = reinterpret_cast<float*>(ws);
+  a.out = out;
+  // one split per sequence: the decode kernel writes the output itself and the combine launch
+  // is skipped (DIRECTKV_DECODE_COMBINE=1 keeps the combine, which gives bitwise the same output)
+  const char* force_combine = getenv("DIRECTKV_DECODE_COMBINE");
+  a.direct = p.n_splits == batch && !(force_combine && force_combine[0] == '1');
   a.qf = decode_uses_qpass(c, p, batch, n_q_heads, D)
              ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + decode_part_bytes(c, batch, n_q_heads, paged))
              : nullptr;
@@ -340,8 +345,7 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   if (a.qf && (e = fq(a, s)) != hipSuccess) return hip_fail(e, "query projection launch");
   e = fd(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  e = fc(ca, s);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (!a.direct && (e = fc(ca, s)) != hipSuccess) return hip_fail(e, "combine launch");
   return DKV_OK;
 }
 

@@ -338,9 +338,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       acc = fmaf(s_o[(sl * G + h) * DH + i], w, acc);
       lsum = fmaf(s_l[sl * G + h], w, lsum);
     }
-    float* ph = part + (size_t)h * (DH + 2);
-    ph[i] = acc;
-    if (i == 0) { ph[DH] = M; ph[DH + 1] = lsum; }
+    if (a.direct) {
+      // the only split of this sequence: its merged state is the output (what the combine
+      // would compute from it, with weight 2^0 = 1)
+      T* orow = reinterpret_cast<T*>(a.out) + ((size_t)b * a.Hq + (size_t)g * G + h) * DH;
+      orow[i] = Elem<T>::from_float(acc / lsum);
+    } else {
+      float* ph = part + (size_t)h * (DH + 2);
+      ph[i] = acc;
+      if (i == 0) { ph[DH] = M; ph[DH + 1] = lsum; }
+    }
   }
 }
 

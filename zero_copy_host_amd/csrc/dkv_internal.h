@@ -142,6 +142,9 @@ struct DecodeArgs {
   void* kc;                 // host cache
   void* vc;
   float* part;              // [n_splits_total][Hq][d + 2]: o (unnormalised), m, l
+  void* out;                // [B, Hq*d]: written here directly when `direct`
+  int32_t direct;           // 1: every sequence has one split, whose merged state is the output
+                            // (no partials, no combine launch)
   float* qf;                // [B][Hq*d] queries projected once per step and pre-scaled by
                             // log2(e)/sqrt(d), or null: each workgroup projects its own
   int32_t B, D, Hq, Hkv, cap, n_splits;
