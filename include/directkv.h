@@ -45,6 +45,18 @@
 extern "C" {
 #endif
 
+/*
+ * Environment variables read at each call (tuning and testing only; results are unchanged
+ * except where stated):
+ *   DIRECTKV_PREFILL_CHUNK=<keys>  keys per prefill super-chunk (rounded down to a multiple of
+ *                                  64), instead of the L2-sized default; rounding order of the
+ *                                  attention changes, not the result within tolerance;
+ *   DIRECTKV_DECODE_QPASS=0|1      decode q projected inside the attention kernel (0) or by the
+ *                                  pre-pass (1); bitwise the same queries;
+ *   DIRECTKV_DECODE_COMBINE=1      keep the combine launch when every sequence has one split;
+ *                                  bitwise the same output.
+ */
+
 typedef enum { DKV_F32 = 0, DKV_F16 = 1, DKV_BF16 = 2 } dkv_dtype;
 
 typedef enum {
