@@ -215,3 +215,43 @@ def draw_layer(seed: int, B: int, T: int, past, D: int, Hq: int, Hkv: int, d: in
     fill_past(dr, kp, vp, past_len, dtype)
     return dict(wq=wq, wk=wk, wv=wv, x=x, past_len=past_len, kp=kp, vp=vp, dtype=dtype,
                 B=B, T=T, D=D, Hq=Hq, Hkv=Hkv, d=d, cap=cap)
+
+
+def grid(a: np.ndarray, step: float, lim: float) -> np.ndarray:
+    """Values on the grid of multiples of `step`, clipped to [-lim, lim] (input encoding: with
+    step and lim powers of two and lim/step <= 128, every value is exact in bf16, f16 and f32)."""
+    return np.clip(np.round(np.asarray(a, dtype=np.float64) / step) * step, -lim, lim).astype(np.float32)
+
+
+def draw_layer_large_scores(seed: int, B: int, T: int, past, D: int, Hq: int, Hkv: int, d: int, dtype: str,
+                            cap: int, x_max: int = 16, k_lo: float = 0.5, k_hi: float = 4.0,
+                            past_lo: int = 0, past_hi: int = 0):
+    """Inputs with large attention scores that grow along the key positions, for the softmax's
+    running maximum: it is raised again and again across key tiles and launches.
+
+    Every stored input and every product the layer forms from them is exact in all three dtypes:
+    X holds integers in [-x_max, x_max]; Wq has 8 entries of +-1 per column (so |Q| <= 8 x_max,
+    integers); Wk and Wv have 8 entries of +-1/16 and +-1/32 per column; past K is N(0,1) times a
+    ramp that grows geometrically from k_lo at key 0 to k_hi at the last past key, and past V is
+    N(0,1), both on the grid of 1/16 within [-8, 8]. With x_max <= 16 the query-key dot products
+    are multiples of 1/16 below 2^21, exact in fp32, so the only rounding in the scores is their
+    scaling. Draw order: Wq, Wk, Wv, lengths (if ragged), X, past K, past V."""
+    dr = Draw(seed)
+    wq = sparse_sign_weights(dr, D, Hq * d)
+    wk = sparse_sign_weights(dr, D, Hkv * d) / np.float32(16)
+    wv = sparse_sign_weights(dr, D, Hkv * d) / np.float32(32)
+    past_len = dr.lengths(B, past_lo, past_hi) if past is None else np.asarray(past, dtype=np.int32)
+    x = dr.integers((B, T, D), -x_max, x_max)
+    kp = np.zeros((B, Hkv, cap, d), dtype=np.float32)
+    vp = np.zeros((B, Hkv, cap, d), dtype=np.float32)
+    for b in range(B):
+        L = int(past_len[b])
+        ramp = (k_lo * (k_hi / k_lo) ** (np.arange(L) / max(L - 1, 1))).astype(np.float32)[:, None]
+        for g in range(Hkv):
+            kp[b, g, :L] = grid(dr.rng.standard_normal((L, d), dtype=np.float32) * ramp, 1 / 16, 8)
+    for b in range(B):
+        L = int(past_len[b])
+        for g in range(Hkv):
+            vp[b, g, :L] = grid(dr.rng.standard_normal((L, d), dtype=np.float32), 1 / 16, 8)
+    return dict(wq=wq, wk=wk, wv=wv, x=x, past_len=past_len, kp=kp, vp=vp, dtype=dtype,
+                B=B, T=T, D=D, Hq=Hq, Hkv=Hkv, d=d, cap=cap)

@@ -147,11 +147,9 @@ def test_workspace_sizes(dkv):
     ws = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
     e = 2
     # queries + new K + new V + fp32 running state: per 32 query rows, 64 lanes x
-    # (d/32 * 16 accumulators + m + l); then the persistent launches' counters: 8 queue heads,
-    # 8 x 128 query tiles (256 rows each) and an error word
+    # (d/32 * 16 accumulators + m + l)
     want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
-    want += (8 + 8 * 128 + 1) * 4
-    assert want <= ws <= want + 5 * 256
+    assert want <= ws <= want + 4 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
     # decode: fp32 partials (o, m, l) for at most 2 * (2 * 256 / Hkv) + B + 1 splits (the split
     # target doubles for short chunks), then the fp32 queries [B][Hq*d] the pre-pass projects
@@ -258,3 +256,80 @@ def test_disabled_persistent_prefill_is_refused_before_any_launch(dkv):
     x = w = out = ws = 0x10000
     assert L.attn_prefill_variant(ctypes.byref(c), x, w, w, w, lp, 1, 64, 256, 32, out, ws, 1 << 30, None, 4) == -3
     assert "disabled" in _err(dkv)
+
+
+# ---- the Python binding refuses unusable tensors before any library call
+
+def _fake_host_cache(dkv, B=2, Hkv=2, d=128, cap=128, dtype="bf16", live=True):
+    import types
+    c = _fake_cache(dkv, B=B, Hkv=Hkv, d=d, cap=cap, dtype=dkv.DTYPE_CODES[dtype])
+    if not live:
+        c.reserved = 0
+    return types.SimpleNamespace(desc=c, dtype=dtype, shape=(B, Hkv, cap, d))
+
+
+def _layer_tensors(B=2, T=8, D=256, Hq=4, Hkv=2, d=128, dtype=None):
+    import torch
+    dt = dtype or torch.bfloat16
+    return dict(x=torch.zeros(B, T, D, dtype=dt), wq=torch.zeros(Hq * d, D, dtype=dt),
+                wk=torch.zeros(Hkv * d, D, dtype=dt), wv=torch.zeros(Hkv * d, D, dtype=dt),
+                out=torch.zeros(B, T, Hq * d, dtype=dt), ws=torch.zeros(1024, dtype=torch.uint8))
+
+
+def _prefill(dkv, cache, t, Hq=4):
+    dkv.attn_prefill(cache, t["x"], t["wq"], t["wk"], t["wv"], [0, 0], Hq, t["out"], t["ws"])
+
+
+def test_binding_refuses_host_tensors(dkv):
+    """Tensors in host memory would make the kernels read pageable memory: refused."""
+    cache = _fake_host_cache(dkv)
+    t = _layer_tensors()
+    with pytest.raises(ValueError, match="must be a device"):
+        _prefill(dkv, cache, t)
+    with pytest.raises(ValueError, match="must be a device"):
+        dkv.attn_decode(cache, t["x"][:, :1].contiguous(), t["wq"], t["wk"], t["wv"], [0, 0], 4,
+                        t["out"][:, :1].contiguous(), t["ws"])
+    with pytest.raises(ValueError, match="must be a device"):
+        dkv.kv_append(cache, t["x"], t["wk"], t["wv"], [0, 0])
+
+
+def test_binding_refuses_wrong_dtype_shape_layout(dkv):
+    import torch
+    cache = _fake_host_cache(dkv)
+    t = _layer_tensors()
+    bad = dict(t, x=t["x"].float())                              # f32 activations, bf16 cache
+    with pytest.raises(ValueError, match="dtype"):
+        _prefill(dkv, cache, bad)
+    bad = dict(t, wk=torch.zeros(2 * 128, 128, dtype=torch.bfloat16))   # wrong reduction width
+    with pytest.raises(ValueError, match="shape"):
+        _prefill(dkv, cache, bad)
+    bad = dict(t, wq=torch.zeros(256, 4 * 128, dtype=torch.bfloat16).t())   # a transposed view
+    with pytest.raises(ValueError, match="contiguous"):
+        _prefill(dkv, cache, bad)
+    bad = dict(t, out=torch.zeros(2, 7, 512, dtype=torch.bfloat16))   # too small for T = 8
+    with pytest.raises(ValueError, match="elements"):
+        _prefill(dkv, cache, bad)
+    bad = dict(t, ws=[0] * 16)
+    with pytest.raises(TypeError, match="torch tensor"):
+        _prefill(dkv, cache, bad)
+    with pytest.raises(ValueError, match="live cache"):
+        _prefill(dkv, _fake_host_cache(dkv, live=False), t)
+    with pytest.raises(ValueError, match="live cache"):
+        _prefill(dkv, object(), t)
+
+
+def test_binding_refuses_bad_decode_loop_tensors(dkv):
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must be a device"):
+        dkv.rmsnorm(x, torch.zeros(256, dtype=torch.bfloat16), x)
+    with pytest.raises(ValueError, match="shape"):
+        dkv.rmsnorm(x, torch.zeros(128, dtype=torch.bfloat16), x)
+    with pytest.raises(ValueError, match="dtype"):
+        dkv.linear(x, torch.zeros(64, 256, dtype=torch.float16), torch.zeros(4, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="elements"):
+        dkv.linear(x, torch.zeros(64, 256, dtype=torch.bfloat16), torch.zeros(4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="must be a device"):
+        dkv.swiglu(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="unsupported dtype"):
+        dkv.swiglu(torch.zeros(4, 64, dtype=torch.int32), torch.zeros(4, 32, dtype=torch.int32))

@@ -112,6 +112,69 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+_CODE_NAMES = {v: k for k, v in DTYPE_CODES.items()}
+
+
+def _torch_code(t) -> Optional[int]:
+    import torch
+    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}.get(t.dtype)
+
+
+def _tensor(t, name: str, code: Optional[int] = None, shape=None, numel: Optional[int] = None,
+            device: bool = True):
+    """Refuse, before any library call, a tensor the kernels could not use safely: not a
+    torch tensor, not contiguous, of another dtype than the call's, of the wrong shape or size,
+    or (device=True) not in device memory (the kernels would read pageable host memory or out of
+    bounds)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if code is not None and _torch_code(t) != code:
+        raise ValueError(f"{name} has dtype {t.dtype}; this call computes in {_CODE_NAMES[code]}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor, got one on {t.device}")
+    return t
+
+
+def _tensors(*specs) -> None:
+    """_tensor over several (tensor, name, kwargs) specs: every layout check first, then the
+    placement of each, so that the message names the first real mismatch."""
+    for t, name, kw in specs:
+        _tensor(t, name, device=False, **kw)
+    for t, name, kw in specs:
+        _tensor(t, name, **kw)
+
+
+def _cache_desc(cache, kind):
+    """The live descriptor of a HostKVCache / PagedHostKVCache (refuses a freed cache)."""
+    desc = getattr(cache, "desc", None)
+    if not isinstance(desc, kind) or not desc.reserved:
+        raise ValueError("cache is not a live cache made by this library (freed, or another object)")
+    return desc
+
+
+def _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads: int, T: int, B: int, D: int, n_kv_heads: int,
+                   head_dim: int) -> None:
+    """Dtype, shape and placement of the tensors of a layer call (wq / out may be None for an append)."""
+    code = DTYPE_CODES[cache.dtype]
+    specs = [(x, "x", dict(code=code, shape=(B, D) if (x.dim() == 2 and T == 1) else (B, T, D)))]
+    if wq is not None:
+        specs.append((wq, "wq", dict(code=code, shape=(n_q_heads * head_dim, D))))
+    specs += [(wk, "wk", dict(code=code, shape=(n_kv_heads * head_dim, D))),
+              (wv, "wv", dict(code=code, shape=(n_kv_heads * head_dim, D)))]
+    if out is not None:
+        specs.append((out, "out", dict(code=code, numel=B * T * n_q_heads * head_dim)))
+    if ws is not None:
+        specs.append((ws, "ws", {}))
+    _tensors(*specs)
+
+
 def _lens(past_len, batch: int):
     a = np.ascontiguousarray(np.asarray(past_len, dtype=np.int32))
     if a.shape != (batch,):
@@ -169,8 +232,10 @@ class HostKVCache:
 def kv_append(cache: HostKVCache, x, wk, wv, past_len: Sequence[int], stream=None) -> None:
     """Append round(X·Wkᵀ), round(X·Wvᵀ) at rows [past_len[b], past_len[b]+T). x: [B, T, D]."""
     B, T, D = x.shape
+    desc = _cache_desc(cache, dkv_cache)
+    _layer_tensors(cache, x, None, wk, wv, None, None, 0, T, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
-    _check(lib().kv_append(ctypes.byref(cache.desc), _ptr(x), _ptr(wk), _ptr(wv), lp, B, T, D, _stream(stream)))
+    _check(lib().kv_append(ctypes.byref(desc), _ptr(x), _ptr(wk), _ptr(wv), lp, B, T, D, _stream(stream)))
 
 
 def workspace_bytes(phase: str, cache: HostKVCache, batch: int, T: int, n_q_heads: int) -> int:
@@ -183,19 +248,23 @@ def workspace_bytes(phase: str, cache: HostKVCache, batch: int, T: int, n_q_head
 def attn_prefill(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:
     """One prefill step of T tokens per sequence; out: [B, T, Hq*d] device tensor."""
     B, T, D = x.shape
+    desc = _cache_desc(cache, dkv_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, T, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().attn_prefill(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T, D,
+    _check(lib().attn_prefill(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T, D,
                               n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
 def attn_prefill_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, variant: str,
                          stream=None) -> None:
-    """attn_prefill with the host cache read as `variant` ("fused", "naive", "separate")."""
+    """attn_prefill with the host cache read as `variant` ("fused", "naive", "separate", "staged")."""
     B, T, D = x.shape
+    desc = _cache_desc(cache, dkv_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, T, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().attn_prefill_variant(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T,
+    _check(lib().attn_prefill_variant(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T,
                                       D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream),
                                       PREFILL_VARIANTS[variant]))
 
@@ -203,9 +272,11 @@ def attn_prefill_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads:
 def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:
     """One decode step; x: [B, 1, D] (or [B, D]); out: [B, 1, Hq*d] device tensor."""
     B, D = x.shape[0], x.shape[-1]
+    desc = _cache_desc(cache, dkv_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, 1, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().attn_decode(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
+    _check(lib().attn_decode(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
                              n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
@@ -295,10 +366,12 @@ def paged_workspace_bytes(phase: str, cache: PagedHostKVCache, batch: int, T: in
 def kv_paged_append(cache: PagedHostKVCache, table, x, wk, wv, past_len, ws, stream=None) -> None:
     """kv_append into the pages the block table names. x: [B, T, D]."""
     B, T, D = x.shape
+    desc = _cache_desc(cache, dkv_paged_cache)
+    _layer_tensors(cache, x, None, wk, wv, None, ws, 0, T, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     t, tp, mp = _table(table, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().kv_paged_append(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wk), _ptr(wv), lp, B, T, D,
+    _check(lib().kv_paged_append(ctypes.byref(desc), tp, mp, _ptr(x), _ptr(wk), _ptr(wv), lp, B, T, D,
                                  _ptr(ws), nbytes, _stream(stream)))
 
 
@@ -306,10 +379,12 @@ def attn_prefill_paged(cache: PagedHostKVCache, table, x, wq, wk, wv, past_len, 
                        stream=None) -> None:
     """attn_prefill on a paged cache; out: [B, T, Hq*d] device tensor."""
     B, T, D = x.shape
+    desc = _cache_desc(cache, dkv_paged_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, T, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     t, tp, mp = _table(table, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().attn_prefill_paged(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
+    _check(lib().attn_prefill_paged(ctypes.byref(desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
                                     B, T, D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
@@ -317,10 +392,12 @@ def attn_decode_paged(cache: PagedHostKVCache, table, x, wq, wk, wv, past_len, n
                       stream=None) -> None:
     """attn_decode on a paged cache; x: [B, 1, D] (or [B, D]); out: [B, 1, Hq*d]."""
     B, D = x.shape[0], x.shape[-1]
+    desc = _cache_desc(cache, dkv_paged_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, 1, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     t, tp, mp = _table(table, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().attn_decode_paged(ctypes.byref(cache.desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
+    _check(lib().attn_decode_paged(ctypes.byref(desc), tp, mp, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp,
                                    B, D, n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
@@ -328,23 +405,30 @@ def attn_decode_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: 
                         stream=None) -> None:
     """attn_decode reading the cache as `variant` ("zerocopy", or "staged": DMA into device memory first)."""
     B, D = x.shape[0], x.shape[-1]
+    desc = _cache_desc(cache, dkv_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, 1, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     nbytes = ws.numel() * ws.element_size()
-    _check(lib().attn_decode_variant(ctypes.byref(cache.desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
+    _check(lib().attn_decode_variant(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
                                      n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream),
                                      DECODE_VARIANTS[variant]))
 
 
 def _dtype_code(t) -> int:
-    import torch
-    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[t.dtype]
+    code = _torch_code(t)
+    if code is None:
+        raise ValueError(f"unsupported dtype {t.dtype} (float32, float16, bfloat16)")
+    return code
 
 
 def rmsnorm(x, weight, y, eps: float = 1e-5, stream=None) -> None:
     """y = x / sqrt(mean(x^2) + eps) * weight over the last axis; y may be x."""
     D = x.shape[-1]
     rows = x.numel() // D
-    _check(lib().dkv_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), rows, D, eps, _dtype_code(x), _stream(stream)))
+    code = _dtype_code(x)
+    _tensors((x, "x", dict(code=code)), (weight, "weight", dict(code=code, shape=(D,))),
+             (y, "y", dict(code=code, numel=x.numel())))
+    _check(lib().dkv_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), rows, D, eps, code, _stream(stream)))
 
 
 def linear(x, w, y, residual=None, stream=None) -> None:
@@ -352,15 +436,24 @@ def linear(x, w, y, residual=None, stream=None) -> None:
     K = x.shape[-1]
     rows = x.numel() // K
     N = w.shape[0]
-    _check(lib().dkv_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), rows, N, K, _dtype_code(x),
-                            _stream(stream)))
+    code = _dtype_code(x)
+    specs = [(x, "x", dict(code=code)), (w, "w", dict(code=code, shape=(N, K))),
+             (y, "y", dict(code=code, numel=rows * N))]
+    if residual is not None:
+        specs.append((residual, "residual", dict(code=code, numel=rows * N)))
+    _tensors(*specs)
+    _check(lib().dkv_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), rows, N, K, code, _stream(stream)))
 
 
 def swiglu(gate_up, y, stream=None) -> None:
     """y = silu(gate) * up for gate_up = [gate, up] on the last axis."""
     F2 = gate_up.shape[-1]
     rows = gate_up.numel() // F2
-    _check(lib().dkv_swiglu(_ptr(gate_up), _ptr(y), rows, F2 // 2, _dtype_code(gate_up), _stream(stream)))
+    code = _dtype_code(gate_up)
+    if F2 % 2:
+        raise ValueError(f"gate_up's last axis ({F2}) must hold the gate and up halves")
+    _tensors((gate_up, "gate_up", dict(code=code)), (y, "y", dict(code=code, numel=rows * (F2 // 2))))
+    _check(lib().dkv_swiglu(_ptr(gate_up), _ptr(y), rows, F2 // 2, code, _stream(stream)))
 
 
 def hostlink_stream(host_ptr: int, nbytes: int, mode: str, n_wg: int = 1024, stream=None) -> None:

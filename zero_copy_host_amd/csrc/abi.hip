@@ -45,6 +45,36 @@ size_t elem_size(int dtype) { return dtype == DKV_F32 ? 4 : 2; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// `p` must be the start of (or lie inside) a pinned host allocation from hipHostMalloc that
+// holds `bytes` bytes from p on: device memory, pageable memory and allocations too small for
+// the descriptor's shape are refused before a kernel could dereference them. The HIP runtime
+// keeps the allocation map; a failed query leaves no error behind for a later launch check.
+int check_host_buffer(const void* p, size_t bytes, const char* what) {
+  hipPointerAttribute_t at;
+  memset(&at, 0, sizeof(at));
+  hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DKV_ERR_INVALID_ARG, "%s is not memory the HIP runtime knows (pageable host memory?): %s", what,
+                hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeHost)
+    return fail(DKV_ERR_INVALID_ARG, "%s is not pinned host memory (hipMemoryType %d)", what, (int)at.type);
+  hipDeviceptr_t start = nullptr;
+  size_t size = 0;
+  if (hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, const_cast<void*>(p)) == hipSuccess &&
+      hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, const_cast<void*>(p)) == hipSuccess &&
+      size > 0) {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(start), q = reinterpret_cast<uintptr_t>(p);
+    if (q < s0 || q - s0 > size || size - (q - s0) < bytes)
+      return fail(DKV_ERR_INVALID_ARG, "%s: the pinned allocation holds %zu bytes from this pointer, the cache needs %zu",
+                  what, size - std::min<size_t>(size, q - s0), bytes);
+  } else {
+    (void)hipGetLastError();   // no range information: the memory type check above stands alone
+  }
+  return DKV_OK;
+}
+
 int check_cache(const dkv_cache* c) {
   if (!c) return fail(DKV_ERR_INVALID_ARG, "cache descriptor is null");
   if (c->reserved != kMagic || !c->k || !c->v)
@@ -55,6 +85,15 @@ int check_cache(const dkv_cache* c) {
   if (c->batch <= 0 || c->n_kv_heads <= 0 || c->capacity <= 0)
     return fail(DKV_ERR_INVALID_ARG, "cache sizes must be positive");
   return DKV_OK;
+}
+
+// The memory behind a cache descriptor, checked after every argument check and before the
+// first enqueue: k and v are pinned host allocations of the descriptor's size.
+int check_cache_memory(const dkv_cache* c) {
+  const size_t bytes = (size_t)c->batch * c->n_kv_heads * c->capacity * c->head_dim * elem_size(c->dtype);
+  int st = check_host_buffer(c->k, bytes, "cache k");
+  if (st) return st;
+  return check_host_buffer(c->v, bytes, "cache v");
 }
 
 // common checks of a layer call; T new tokens per sequence
@@ -92,17 +131,29 @@ int check_heads(const dkv_cache* c, int32_t n_q_heads) {
   return DKV_OK;
 }
 
-// ---- device facts, queried once per process
-int g_cus = 0;
+// ---- device facts, queried once per process (the first device a call runs on)
+int g_cus = 0, g_xccs = 0;
 std::once_flag g_dev_once;
-int cu_count() {
+void query_device() {
   std::call_once(g_dev_once, [] {
     int dev = 0;
     hipDeviceProp_t p;
     if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess) g_cus = p.multiProcessorCount;
+    if (hipDeviceGetAttribute(&g_xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) g_xccs = 0;
+    (void)hipGetLastError();
     if (g_cus <= 0) g_cus = 256;
   });
+}
+int cu_count() {
+  query_device();
   return g_cus;
+}
+// The prefill places pairs on XCDs by workgroup index (workgroup i runs on XCD i % 8), which
+// holds on the whole MI355X: 256 CUs in 8 XCDs. A partitioned device reports fewer; there the
+// placement would only cost L2 reuse, and it is switched off.
+bool xcd_placement() {
+  query_device();
+  return g_cus == 256 && g_xccs == 8;
 }
 
 // ---- decode plan: equal key chunks for every workgroup, whatever the lengths
@@ -121,7 +172,7 @@ constexpr int kDecodeWgPerCu = 2;
 constexpr int64_t kShortChunk = 1024;
 
 int decode_target_splits(const dkv_cache* c) {
-  return std::max(1, kDecodeWgPerCu * 256 / c->n_kv_heads);
+  return std::max(1, kDecodeWgPerCu * cu_count() / c->n_kv_heads);
 }
 
 void plan_decode(const dkv_cache* c, const int32_t* past_len, int32_t batch, bool paged, DecodePlan& p) {
@@ -176,7 +227,7 @@ bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, i
 
 // ---- prefill workspace layout
 struct PrefillWs {
-  size_t q, k_new, v_new, state, sync, total;
+  size_t q, k_new, v_new, state, total;
 };
 
 PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
@@ -187,10 +238,7 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   w.k_new = w.q + round_up((size_t)batch * T * n_q_heads * d * e, 256);
   w.v_new = w.k_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
   w.state = w.v_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
-  w.sync = w.state + round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
-  // persistent launches: 8 queue heads, 8 x q_tiles completion counters, an error word
-  const size_t q_tiles = ((size_t)T * std::max(1, G) + attn_rows_per_tile() - 1) / attn_rows_per_tile();
-  w.total = w.sync + round_up((8 + 8 * q_tiles + 1) * sizeof(int32_t), 256);
+  w.total = w.state + round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
   return w;
 }
 
@@ -397,40 +445,13 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   const int rows = attn_rows_per_tile();
   aa.q_tiles = (T * G + rows - 1) / rows;
   const int P = batch * c->n_kv_heads;
-  aa.xcd_group = variant != DKV_PREFILL_NAIVE && P >= 8;
+  aa.xcd_group = variant != DKV_PREFILL_NAIVE && P >= 8 && xcd_placement();
   aa.new_from_host = separate;
   for (int b = 0; b < batch; ++b) aa.past_len[b] = past_len[b];
   // With a multiple of 8 pairs, the pairs go in groups of 8, one pair per XCD: each XCD's L2
   // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which
   // halves the launches every query tile makes and the running-state traffic they cost.
   const int group = aa.xcd_group && P % 8 == 0 ? 8 : P;
-  // (the persistent launch picks its queue by XCC id: it assumes one device of 8 XCDs of 32 CUs,
-  // the unpartitioned MI355X; on anything else the fused path runs)
-  if (variant == DKV_PREFILL_PERSIST && !paged && group == 8 && cu_count() == 256) {
-    // one persistent launch per group: each XCD holds the super-chunk it computes and the one
-    // its producer item brings in, so a super-chunk is half the per-launch size
-    attn_fn fpz = find_attn_persist(c->dtype, c->head_dim, G);
-    if (!fpz) return fail(DKV_ERR_UNSUPPORTED, "no persistent instance for dtype %d d %d G %d", c->dtype, c->head_dim, G);
-    int32_t* sync = reinterpret_cast<int32_t*>(w + lay.sync);
-    const int n_sync = 8 + 8 * aa.q_tiles + 1;
-    aa.queue = sync;
-    aa.done = sync + 8;
-    aa.error = sync + 8 + 8 * aa.q_tiles;
-    aa.pre_slot = std::min(std::max(1, cu_count() / 8), aa.q_tiles);
-    for (int pair0 = 0; pair0 < P; pair0 += 8) {
-      int max_keys = 0;
-      for (int b = pair0 / c->n_kv_heads; b <= (pair0 + 7) / c->n_kv_heads; ++b)
-        max_keys = std::max(max_keys, past_len[b] + T);
-      aa.pair0 = pair0;
-      aa.pairs = 8;
-      aa.sk = superchunk_keys(c, 8, true, aa.q_tiles);   // the quarter-L2 budget: two super-chunks resident
-      aa.max_keys = max_keys;
-      aa.n_sc = (max_keys + aa.sk - 1) / aa.sk;
-      if ((e = launch_zero_ints(sync, n_sync, s)) != hipSuccess) return hip_fail(e, "counter reset");
-      if ((e = fpz(aa, s)) != hipSuccess) return hip_fail(e, "attention launch");
-    }
-    return DKV_OK;
-  }
   for (int pair0 = 0; pair0 < P; pair0 += group) {
     aa.pair0 = pair0;
     aa.pairs = group;
@@ -566,6 +587,14 @@ int check_paged(const dkv_paged_cache* pc) {
     return fail(DKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", pc->head_dim);
   if (pc->n_pages <= 0 || pc->n_kv_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "paged cache sizes must be positive");
   return DKV_OK;
+}
+
+// the page pools are pinned host allocations of n_pages pages (checked before the first enqueue)
+int check_paged_memory(const dkv_paged_cache* pc) {
+  const size_t bytes = (size_t)pc->n_pages * pc->n_kv_heads * kPageTokens * pc->head_dim * elem_size(pc->dtype);
+  int st = check_host_buffer(pc->k, bytes, "page pool k");
+  if (st) return st;
+  return check_host_buffer(pc->v, bytes, "page pool v");
 }
 
 // a dkv_cache view of a page pool for one call: capacity is what the table can address
@@ -711,6 +740,7 @@ int kv_append(const dkv_cache* c, const void* x, const void* wk, const void* wv,
   int st = check_call(c, batch, T, D, past_len, {x, wk, wv});
   if (st) return st;
   if (T == 0) return DKV_OK;
+  if ((st = check_cache_memory(c))) return st;
   return run_append(c, Paging{}, x, wk, wv, past_len, batch, T, D, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -742,11 +772,13 @@ int attn_decode_variant(const dkv_cache* c, const void* x, const void* wq, const
   if (variant != DKV_DECODE_ZEROCOPY && variant != DKV_DECODE_STAGED)
     return fail(DKV_ERR_INVALID_ARG, "unknown decode variant %d", variant);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (variant == DKV_DECODE_ZEROCOPY)
-    return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes, s);
-  const size_t sb = 2 * staging_bytes(c), need = sb + decode_ws_bytes(c, batch, n_q_heads, false);
+  const size_t sb = variant == DKV_DECODE_STAGED ? 2 * staging_bytes(c) : 0;
+  const size_t need = sb + decode_ws_bytes(c, batch, n_q_heads, false);
   if (!ws || ws_bytes < need || !aligned16(ws))
     return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  if ((st = check_cache_memory(c))) return st;
+  if (variant == DKV_DECODE_ZEROCOPY)
+    return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes, s);
   const dkv_cache dev = staged_view(c, ws);
   if ((st = stage_in(c, dev, past_len, s))) return st;
   if ((st = run_decode(&dev, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out,
@@ -770,17 +802,20 @@ int attn_prefill_variant(const dkv_cache* c, const void* x, const void* wq, cons
   if ((st = check_heads(c, n_q_heads))) return st;
   if (variant < DKV_PREFILL_FUSED || variant > DKV_PREFILL_PERSIST)
     return fail(DKV_ERR_INVALID_ARG, "unknown prefill variant %d", variant);
-  // The persistent launch did not complete on the GPU (its run never returned, also with every
-  // wait bounded); the cause is not found, so the variant is refused until it is.
+  // The persistent launch (workgroups handing the running state to each other through counters)
+  // did not complete on the GPU and its cause was not found: it is disabled and no longer built.
   if (variant == DKV_PREFILL_PERSIST)
-    return fail(DKV_ERR_UNSUPPORTED, "DKV_PREFILL_PERSIST is disabled: its launch did not complete on the GPU");
+    return fail(DKV_ERR_UNSUPPORTED, "DKV_PREFILL_PERSIST is disabled (not built): its launch did not complete on "
+                                     "the GPU");
   if (T == 0) return DKV_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (variant != DKV_PREFILL_STAGED)
-    return run_prefill(c, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes, s, variant);
-  const size_t sb = 2 * staging_bytes(c), need = sb + prefill_layout(c, batch, T, n_q_heads).total;
+  const size_t sb = variant == DKV_PREFILL_STAGED ? 2 * staging_bytes(c) : 0;
+  const size_t need = sb + prefill_layout(c, batch, T, n_q_heads).total;
   if (!ws || ws_bytes < need || !aligned16(ws))
     return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  if ((st = check_cache_memory(c))) return st;
+  if (variant != DKV_PREFILL_STAGED)
+    return run_prefill(c, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes, s, variant);
   const dkv_cache dev = staged_view(c, ws);
   if ((st = stage_in(c, dev, past_len, s))) return st;
   if ((st = run_prefill(&dev, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out,
@@ -856,6 +891,7 @@ int kv_paged_append(const dkv_paged_cache* c, const int32_t* block_table, int32_
   if (st) return st;
   if ((st = check_call(&view, batch, T, D, past_len, {x, wk, wv}))) return st;
   if (T == 0) return DKV_OK;
+  if ((st = check_paged_memory(c))) return st;
   hipError_t e;
   pg = stage_table(block_table, batch, max_pages, ws, s, e);
   if (e != hipSuccess) return hip_fail(e, "block table copy");
@@ -882,6 +918,7 @@ int attn_decode_paged(const dkv_paged_cache* c, const int32_t* block_table, int3
   if ((st = check_call(&view, batch, 1, D, past_len, {x, wq, wk, wv, out}))) return st;
   if ((st = check_heads(&view, n_q_heads))) return st;
   if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
+  if ((st = check_paged_memory(c))) return st;
   hipError_t e;
   pg = stage_table(block_table, batch, max_pages, ws, s, e);
   if (e != hipSuccess) return hip_fail(e, "block table copy");
@@ -909,6 +946,7 @@ int attn_prefill_paged(const dkv_paged_cache* c, const int32_t* block_table, int
   if ((st = check_call(&view, batch, T, D, past_len, {x, wq, wk, wv, out}))) return st;
   if ((st = check_heads(&view, n_q_heads))) return st;
   if (T == 0) return DKV_OK;
+  if ((st = check_paged_memory(c))) return st;
   hipError_t e;
   pg = stage_table(block_table, batch, max_pages, ws, s, e);
   if (e != hipSuccess) return hip_fail(e, "block table copy");

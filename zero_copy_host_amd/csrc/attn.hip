@@ -444,152 +444,6 @@ void attn_kernel(const AttnArgs a) {
   attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, a.kc1, a.first, a.last});
 }
 
-// ---------------------------------------------------------------- persistent prefill
-// One launch per group of 8 (sequence, kv head) pairs, pair pair0 + x on XCD x, with a work
-// queue per XCD: for each key super-chunk s, the items (s, query tile) in heaviest-first order,
-// and after the first round of them a producer item that reads the pair's host rows of
-// super-chunk s + 1 into that XCD's L2. L2 keeps host lines only within one kernel, so here the
-// next super-chunk arrives over the link while this one is computed from L2, instead of in a
-// link-bound first round of its own launch. The running state (o, m, l) of a query tile passes
-// from item (s, qt) to item (s + 1, qt) through device memory: the writer waits for its stores
-// and bumps a per-tile counter with an L2 atomic; the reader polls that counter with an L2
-// atomic as well (a device-scope load is served beyond this XCD's L2 and does not see it) in a
-// bounded wait (items are taken in order, so the item it waits for is held by a running
-// workgroup), then drops its CU's L1 before reading the state. Every workgroup picks its queue from the XCC id register,
-// so writer and reader always share one L2, whatever the placement of workgroups.
-
-// A wait gives up (and flags the error word) after 0.25 s of the 100 MHz real-time clock; a
-// correct run waits at most about one item (well under a millisecond).
-constexpr unsigned long long kWaitTicks = 25000000ull;
-
-// the host rows [j0, j1) of pair p (K and V) are read once and dropped: they stay in L2
-template <typename T, int DH>
-__device__ inline void attn_prefetch(const AttnArgs& a, const int p, const int j0, const int j1) {
-  constexpr int THREADS = AttnCfg<T, DH>::THREADS;
-  const size_t base = ((size_t)p * a.cap + j0) * DH;
-  const size_t n16 = (size_t)(j1 - j0) * DH * sizeof(T) / 16;
-  const uint4* k = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kc) + base);
-  const uint4* v = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.vc) + base);
-  unsigned acc = 0;
-  for (size_t i = threadIdx.x; i < n16; i += 4 * THREADS) {
-    uint4 t[8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t e = min(i + (size_t)u * THREADS, n16 - 1);   // in bounds; repeats are L2 hits
-      t[u] = k[e];
-      t[4 + u] = v[e];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= t[u].x ^ t[u].w;
-  }
-  if (acc == 0x9E3779B9u && a.sk < 0) atomicOr(a.error, (int)acc);   // keeps the loads (never true)
-}
-
-template <typename T, int DH, int G>
-__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
-void attn_persist_kernel(const AttnArgs a) {
-  __shared__ int s_item;
-  const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID: this XCD
-  const int p = a.pair0 + x;
-  const int b = p / a.Hkv;
-  const int L = a.past_len[b];
-  const int Q = a.q_tiles, S = a.n_sc, per_sc = Q + 1;
-  int* const done = a.done + (size_t)x * Q;
-  // the new rows of this pair are written to the host by the items of the super-chunks that
-  // hold none of its host rows, a share each
-  const int s_store = min(S - 1, (L + a.sk - 1) / a.sk);
-  const long long n_store = (long long)(S - s_store) * Q;
-  for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(a.queue + x, 1);
-    __syncthreads();
-    const int item = s_item;
-    __syncthreads();
-    if (item >= S * per_sc) break;
-    const int s = item / per_sc, r = item - s * per_sc;
-    const int kc0 = s * a.sk, kc1 = min(kc0 + a.sk, a.max_keys);
-    if (r == a.pre_slot) {
-      const int n1 = min(kc1 + a.sk, L);
-      if (kc1 < n1) attn_prefetch<T, DH>(a, p, kc1, n1);
-      continue;
-    }
-    const int ci = r < a.pre_slot ? r : r - 1;
-    const int qt = Q - 1 - ci;
-    if (s > 0) {
-      if (threadIdx.x == 0) {
-        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-        // a compare-and-swap that never swaps (the counters are never -1) reads the counter with
-        // an L2 atomic, like the one that publishes (an atomic add of 0 would become a load)
-        while (atomicCAS(done + qt, -1, -1) < s) {
-          __builtin_amdgcn_s_sleep(2);
-          if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-            atomicOr(a.error, 1);
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      asm volatile("buffer_inv sc0" ::: "memory");   // this CU's L1 may hold an older state
-    }
-    if (s >= s_store) {
-      const long long k = (long long)(s - s_store) * Q + ci;
-      const int t0 = (int)(a.T * k / n_store), t1 = (int)(a.T * (k + 1) / n_store);
-      attn_store<T, DH, false>(a, p * a.T + t0, p * a.T + t1);
-    }
-    attn_item<T, DH, G, false>(a, AttnItem{p, qt, kc0, kc1, s == 0, s == S - 1});
-    // publish: this item's state stores have reached L2 before the counter moves
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(done + qt, 1);
-  }
-}
-
-__global__ void zero_ints_kernel(int32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
-hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_ints_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-template <typename T, int DH, int G>
-static hipError_t launch_attn_persist(const AttnArgs& a, hipStream_t s) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int per_xcd = cus / 8 > 0 ? cus / 8 : 1;   // one workgroup per CU
-  hipLaunchKernelGGL((attn_persist_kernel<T, DH, G>), dim3(8 * per_xcd), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename T, int DH>
-static attn_fn pick_persist_g(int G) {
-  switch (G) {
-    case 1: return launch_attn_persist<T, DH, 1>;
-    case 2: return launch_attn_persist<T, DH, 2>;
-    case 4: return launch_attn_persist<T, DH, 4>;
-    case 8: return launch_attn_persist<T, DH, 8>;
-    default: return nullptr;
-  }
-}
-
-template <typename T>
-static attn_fn pick_persist_d(int d, int G) {
-  if (d == 64) return pick_persist_g<T, 64>(G);
-  if (d == 128) return pick_persist_g<T, 128>(G);
-  return nullptr;
-}
-
-attn_fn find_attn_persist(int dtype, int d, int G) {
-  switch (dtype) {
-    case 0: return pick_persist_d<float>(d, G);
-    case 1: return pick_persist_d<_Float16>(d, G);
-    case 2: return pick_persist_d<__bf16>(d, G);
-    default: return nullptr;
-  }
-}
-
 template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int P = a.pairs;

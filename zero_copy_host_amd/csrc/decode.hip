@@ -59,11 +59,15 @@ __device__ void project_rows(const float* __restrict__ sx, const T* __restrict__
   }
 }
 
-// log2(e)/sqrt(d): scores come out in the base-2 exponent domain
-__device__ inline float qproj_scale(int dh) { return 1.4426950408889634f * rsqrtf((float)dh); }
+// log2(e)/sqrt(d). Scores, maxima and partial maxima stay raw dot products q.k; the scale is
+// applied once, to the difference from the maximum, as exp2((s - m) * c): that difference is
+// exact in fp32 for the keys that carry weight (they lie within a factor 2 of the maximum), so
+// the weights keep full fp32 precision however large the scores are. (Scaling q first would
+// round every product and partial sum at the scores' magnitude.)
+__device__ inline float score_scale(int dh) { return 1.4426950408889634f * rsqrtf((float)dh); }
 
 // The queries of a decode step, every (sequence, query head), projected once:
-// qf[b][n] = qproj_scale(d) * sum_k x[b][k] * wq[n][k]. Each weight row streams from HBM once per
+// qf[b][n] = sum_k x[b][k] * wq[n][k]. Each weight row streams from HBM once per
 // BB sequences. The sum over k runs in project_rows' order (lane-strided vectors of VEC, fma in
 // order, then the wave's xor tree), so these are bitwise the values a decode workgroup would
 // compute for itself.
@@ -105,13 +109,12 @@ __global__ __launch_bounds__(256) void qproj_kernel(const DecodeArgs a) {
       }
     }
   }
-  const float scale = qproj_scale(DH);
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int j = 0; j < BB; ++j) {
       const float v = wave_sum(acc[i][j]);
-      if (lane == 0 && j < nb && r0 + i < nrows) a.qf[(size_t)(b0 + j) * nrows + r0 + i] = v * scale;
+      if (lane == 0 && j < nb && r0 + i < nrows) a.qf[(size_t)(b0 + j) * nrows + r0 + i] = v;
     }
 }
 
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     const float* __restrict__ qsrc = a.qf + (size_t)b * a.Hq * DH + (size_t)g * G * DH;
     for (int i = tid; i < G * DH; i += blockDim.x) s_q[i] = qsrc[i];
   } else {
-    project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wq), a.D, g * G * DH, G * DH, s_q, qproj_scale(DH));
+    project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wq), a.D, g * G * DH, G * DH, s_q, 1.f);
   }
   if (has_new) {
     project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wk), a.D, g * DH, DH, s_kv, 1.f);
@@ -192,6 +195,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   }
 
   // ---- stream the host rows
+  const float c = score_scale(DH);
   const int slot = wave * RPW + lane / LPR;
   const int col = (lane % LPR) * VEC;
   float q[G][VEC], o[G][VEC], m[G], l[G];
@@ -248,14 +252,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
       if (mx == -INFINITY) continue;            // nothing valid seen yet
-      const float alpha = exp2f(m[h] - mx);     // exp2(-inf) = 0 on the first update
+      const float alpha = exp2f((m[h] - mx) * c);   // exp2(-inf) = 0 on the first update
       m[h] = mx;
       l[h] *= alpha;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = exp2f(sc[u][h] - mx);
+        const float p = exp2f((sc[u][h] - mx) * c);
         l[h] += p;
         sc[u][h] = p;
       }
@@ -304,8 +308,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
       const float mx = fmaxf(m[h], acc);
-      const float alpha = exp2f(m[h] - mx);
-      const float p = exp2f(acc - mx);
+      const float alpha = exp2f((m[h] - mx) * c);
+      const float p = exp2f((acc - mx) * c);
       m[h] = mx;
       l[h] = l[h] * alpha + p;
 #pragma unroll
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int sl = 0; sl < NSLOT; ++sl) {
       const float ms = s_m[sl * G + h];
       if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
+      const float w = exp2f((ms - M) * c);
       acc = fmaf(s_o[(sl * G + h) * DH + i], w, acc);
       lsum = fmaf(s_l[sl * G + h], w, lsum);
     }
@@ -351,17 +355,19 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   }
 }
 
-// Merge the splits of every (sequence, query head): O = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Merge the splits of every (sequence, query head):
+// O = sum_s o_s 2^((m_s - M) c) / sum_s l_s 2^((m_s - M) c), with raw maxima m_s and c = score_scale.
 template <typename T, int DH>
 __global__ __launch_bounds__(DH) void combine_kernel(const CombineArgs a) {
   const int b = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+  const float c = score_scale(DH);
   const int s0 = a.split_begin[b], s1 = a.split_begin[b + 1];
   float M = -INFINITY;
   for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part[((size_t)s * a.Hq + h) * (DH + 2) + DH]);
   float acc = 0.f, lsum = 0.f;
   for (int s = s0; s < s1; ++s) {
     const float* p = a.part + ((size_t)s * a.Hq + h) * (DH + 2);
-    const float w = exp2f(p[DH] - M);
+    const float w = exp2f((p[DH] - M) * c);
     acc = fmaf(p[i], w, acc);
     lsum = fmaf(p[DH + 1], w, lsum);
   }

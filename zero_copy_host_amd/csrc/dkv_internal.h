@@ -145,8 +145,8 @@ struct DecodeArgs {
   void* out;                // [B, Hq*d]: written here directly when `direct`
   int32_t direct;           // 1: every sequence has one split, whose merged state is the output
                             // (no partials, no combine launch)
-  float* qf;                // [B][Hq*d] queries projected once per step and pre-scaled by
-                            // log2(e)/sqrt(d), or null: each workgroup projects its own
+  float* qf;                // [B][Hq*d] queries projected once per step (fp32, unscaled), or
+                            // null: each workgroup projects its own
   int32_t B, D, Hq, Hkv, cap, n_splits;
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
@@ -183,11 +183,6 @@ struct AttnArgs {
   int32_t store_lo, store_hi;  // (pair, token) rows [store_lo, store_hi) this launch copies
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
-  // persistent prefill: one launch per group of 8 pairs, a work queue per XCD
-  int32_t* queue;           // [8] next item of each XCD's queue (zero at launch)
-  int32_t* done;            // [8][q_tiles] items finished per query tile (zero at launch)
-  int32_t* error;           // set to 1 if a wait gave up (never in a correct run)
-  int32_t sk, n_sc, max_keys, pre_slot;   // keys per super-chunk, super-chunks, key range, producer slot
   int32_t past_len[kMaxBatch];
 };
 
@@ -204,8 +199,6 @@ decode_fn find_decode(int dtype, int d, int G, bool paged);
 combine_fn find_combine(int dtype, int d);
 qproj_fn find_qproj(int dtype, int d);
 attn_fn find_attn(int dtype, int d, int G, bool paged);
-attn_fn find_attn_persist(int dtype, int d, int G);   // contiguous caches, groups of 8 pairs
-hipError_t launch_zero_ints(int32_t* p, int n, hipStream_t s);
 
 int decode_slots(int dtype, int d);  // key rows one decode WG consumes per step
 int attn_rows_per_tile();            // query rows (token x head) per prefill WG

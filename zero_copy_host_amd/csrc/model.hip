@@ -17,10 +17,10 @@ __device__ inline float wsum(float v) {
 }
 
 // y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w, fp32 arithmetic, one rounding at the
-// store. One 256-thread workgroup per row.
+// store. One 256-thread workgroup per row. y may be x (an in-place norm): x and y are not
+// restrict-qualified, and each element is read, then written, by the same thread.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, const T* __restrict__ w,
-                                                      T* __restrict__ y, int D, float eps) {
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __restrict__ w, T* y, int D, float eps) {
   __shared__ float red[4];
   const T* xr = x + (size_t)blockIdx.x * D;
   T* yr = y + (size_t)blockIdx.x * D;
