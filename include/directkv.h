@@ -185,6 +185,21 @@ int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* w
                 int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * attn_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and result as attn_decode
+ * (bitwise), with no workspace argument. Its scratch (split partials and projected queries,
+ * attn_workspace_bytes(1, ...) bytes) lives in a library-owned device array of 8 MiB, one per GPU,
+ * held until the process ends; the call allocates nothing and calls no allocating routine.
+ * Calls that need more scratch than 8 MiB return WORKSPACE (nothing enqueued). Every call on one
+ * GPU uses that GPU's one array: calls that may overlap on a GPU (different streams, or different
+ * host threads without ordering) race on it and must be serialised by the caller. Errors: as
+ * attn_decode, plus WORKSPACE for a call beyond the scratch size.
+ */
+int attn_decode_noalloc(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                        const void* wv, const int32_t* past_len, int32_t batch, int32_t D,
+                        int32_t n_q_heads, void* out, void* stream);
+
+/*
  * attn_decode with the staging baseline selectable: DKV_DECODE_ZEROCOPY is attn_decode;
  * DKV_DECODE_STAGED first copies rows [0, past_len[b]) of every head into a device copy of
  * the cache in the workspace (attn_workspace_bytes phase 3), runs the decode kernels on it,

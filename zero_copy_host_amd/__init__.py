@@ -21,7 +21,7 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HOST_ALLOC",
           -5: "HIP", -6: "WORKSPACE"}
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
-           "attn_prefill_variant", "attn_decode", "attn_decode_variant", "kv_paged_alloc_host", "kv_paged_free_host",
+           "attn_prefill_variant", "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "kv_paged_alloc_host", "kv_paged_free_host",
            "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
            "dkv_rmsnorm", "dkv_linear", "dkv_swiglu", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
 PAGE_TOKENS = 16
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
                                            VP, I32]
         L.attn_decode.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP]
         L.attn_decode_variant.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP, I32]
+        L.attn_decode_noalloc.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP]
         L.kv_paged_alloc_host.argtypes = [P(dkv_paged_cache), I32, I32, I32, I32]
         L.kv_paged_free_host.argtypes = [P(dkv_paged_cache)]
         L.attn_paged_workspace_bytes.argtypes = [I32, P(dkv_paged_cache), I32, I32, I32, I32]
@@ -88,7 +89,7 @@ def lib() -> ctypes.CDLL:
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
         for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
-                     "attn_decode", "attn_decode_variant", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
+                     "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
                      "attn_prefill_paged", "attn_decode_paged", "dkv_rmsnorm", "dkv_linear", "dkv_swiglu",
                      "dkv_hostlink_stream"):
             getattr(L, name).restype = ctypes.c_int
@@ -278,6 +279,17 @@ def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out
     nbytes = ws.numel() * ws.element_size()
     _check(lib().attn_decode(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
                              n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def attn_decode_noalloc(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, stream=None) -> None:
+    """attn_decode with no workspace: the library's own device scratch (8 MiB per GPU) holds the
+    partials, so the call allocates nothing. Calls that may overlap on one GPU must be serialised."""
+    B, D = x.shape[0], x.shape[-1]
+    desc = _cache_desc(cache, dkv_cache)
+    _layer_tensors(cache, x, wq, wk, wv, out, None, n_q_heads, 1, B, D, cache.shape[1], cache.shape[3])
+    lens, lp = _lens(past_len, B)
+    _check(lib().attn_decode_noalloc(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
+                                     n_q_heads, _ptr(out), _stream(stream)))
 
 
 class PagedHostKVCache:

@@ -681,6 +681,36 @@ int paged_front(const dkv_paged_cache* pc, const int32_t* table, int32_t max_pag
   return DKV_OK;
 }
 
+// ---- device-resident scratch for attn_decode_noalloc: a file-scope array, one copy per GPU the
+// library runs on, held until the process ends. Host code never passes the array's name to a
+// kernel (on the host that name is only a stand-in, not a device address): each device's copy
+// is looked up once, with that device current, by hipGetSymbolAddress, and the address kept.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch` (resolved on the first call on that device)
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DKV_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -785,6 +815,27 @@ int attn_decode_variant(const dkv_cache* c, const void* x, const void* wq, const
                        reinterpret_cast<char*>(ws) + sb, ws_bytes - sb, s)))
     return st;
   return stage_out(c, dev, past_len, 1, s);
+}
+
+int attn_decode_noalloc(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                        const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out,
+                        void* stream) {
+  int st = check_call(c, batch, 1, D, past_len, {x, wq, wk, wv, out});
+  if (st) return st;
+  if ((st = check_heads(c, n_q_heads))) return st;
+  if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
+  const size_t need = decode_ws_bytes(c, batch, n_q_heads, false);
+  if (need > kNoAllocScratchBytes)
+    return fail(DKV_ERR_WORKSPACE,
+                "attn_decode_noalloc: this call needs %zu bytes of scratch, the library's device scratch holds %zu "
+                "(use attn_decode with a workspace)", need, kNoAllocScratchBytes);
+  if ((st = check_cache_memory(c))) return st;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws))) return st;
+  // every byte the kernels read from the scratch is written earlier in the same call (the split
+  // partials by the decode kernel, the queries by the projection pre-pass): nothing to clear
+  return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, kNoAllocScratchBytes,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
