@@ -261,10 +261,12 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
         }
       }
     };
-    // mask, tile maximum and the lazy raise of the reference maximum (rescaling o and l)
-    auto rebase = [&](const int j0, Scores& sc) __attribute__((always_inline)) {
+    // mask, tile maximum and the lazy raise of the reference maximum (rescaling o and l);
+    // MASK = false for tiles every row of the workgroup sees whole (the lean path)
+    auto rebase = [&](const int j0, Scores& sc, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       // mask only where some row of this workgroup cannot see some key of the tile
-      if ((j0 + KT > key_hi) || (j0 + KT > key_all)) {
+      if (MASK && ((j0 + KT > key_hi) || (j0 + KT > key_all))) {
 #pragma unroll
         for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
@@ -278,7 +280,7 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      mx = half_max(mx) * sl2;
       // lazy reference maximum: raise it only when a score exceeds it by more than 2^8
       const bool raise = mx > m_run + kLazyRescale;
       if (__any(raise)) {
@@ -292,7 +294,10 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
           for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
       }
     };
-    // Pᵀ = exp2(Sᵀ·scale - m) in operand form, and the row sums into l
+    // Pᵀ = exp2(Sᵀ·scale - m) in operand form, and this lane's share of the row sums into l
+    // (the two lanes of a row, l and l + 32, each sum their own keys; the halves are added when
+    // the output is finalised). 16-bit types sum the rounded weights the PVᵀ product uses, two
+    // per dot2 instruction, so numerator and denominator see the same weights.
     auto probs = [&](const Scores& sc, Probs& pb) __attribute__((always_inline)) {
       const float mref = (m_run == -INFINITY) ? 0.f : m_run;
       float ps = 0.f;
@@ -306,14 +311,13 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
             pb[kb][stp] = w;
           } else {
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) {
-              const float w = __builtin_amdgcn_exp2f(fmaf(sc[kb][stp * KPL + e], sl2, -mref));
-              ps += w;
-              pb[kb][stp][e] = Elem<T>::from_float(w);
-            }
+            for (int e = 0; e < KPL; ++e)
+              pb[kb][stp][e] = Elem<T>::from_float(__builtin_amdgcn_exp2f(fmaf(sc[kb][stp * KPL + e], sl2, -mref)));
+#pragma unroll
+            for (int e = 0; e < KPL; e += 2) ps = Elem<T>::dot2_ones(pb[kb][stp][e], pb[kb][stp][e + 1], ps);
           }
         }
-      l_run += ps + __shfl_xor(ps, 32, 64);
+      l_run += ps;
     };
     // Oᵀ += Vᵀ · Pᵀ; reduction slot (half, e) of step stp is the key held in accumulator
     // register stp*KPL + e of that half, i.e. element e of pb[kb][stp]
@@ -358,7 +362,7 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
     Scores sc;
     auto tile = [&](const int j0, const int buf) __attribute__((always_inline)) {
       qk(sK[buf], sc);
-      rebase(j0, sc);
+      rebase(j0, sc, std::true_type{});
       probs(sc, pb);
       pv(sV[buf], pb);
     };
@@ -383,6 +387,55 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
       __syncthreads();
     };
     int i = 0;
+    // Lean steady state: leading tiles that lie whole inside the launch's keys, are seen whole by
+    // every row of the workgroup (no causal mask), come from one source (the contiguous host cache
+    // or this step's device rows) and whose loads three tiles ahead stay in range too. Their loads
+    // need no clamp, their LDS stores no zero fill and their scores no mask, and the row address
+    // is one uniform tile base plus a fixed per-thread offset.
+    const int n_in = (key_hi - key_lo) / KT;                        // tiles whole inside the range
+    const int n_vis = (max(min(key_hi, key_all), key_lo) - key_lo) / KT;   // and unmasked
+    const bool one_src = !PAGED && (key_hi <= host_end || key_lo >= host_end);
+    const int n_lean = one_src ? (max(0, min(n_vis, n_in - 3)) & ~1) : 0;
+    if (n_lean > 0) {
+      const T* __restrict__ ksrc = key_lo >= host_end ? kn - (size_t)L * DH : kh;   // row j at ksrc + j * DH
+      const T* __restrict__ vsrc = key_lo >= host_end ? vn - (size_t)L * DH : vh;
+      auto gload_lean = [&](int set, int j0) __attribute__((always_inline)) {
+        const T* kt = ksrc + (size_t)j0 * DH;
+        const T* vt = vsrc + (size_t)j0 * DH;
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          rk[set][u] = *reinterpret_cast<const uint4*>(kt + off[u]);
+          rv[set][u] = *reinterpret_cast<const uint4*>(vt + off[u]);
+        }
+      };
+      auto sstore_lean = [&](int buf, int set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          const int kr = krow[u], kc = off[u] - kr * DH;
+          *reinterpret_cast<uint4*>(&sK[buf][kr * LDK + kc]) = rk[set][u];
+          if constexpr (C::VROW) {
+            *reinterpret_cast<uint4*>(&sV[buf][kr * LDV + kc]) = rv[set][u];
+          } else {
+            const T* ve = reinterpret_cast<const T*>(&rv[set][u]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sV[buf][(kc + e) * LDV + kr] = ve[e];
+          }
+        }
+      };
+      auto half_lean = [&](const int i, const int buf, const int set) __attribute__((always_inline)) {
+        sstore_lean(1 - buf, set);
+        gload_lean(set, tj(i + 3));
+        qk(sK[buf], sc);
+        rebase(tj(i), sc, std::false_type{});
+        probs(sc, pb);
+        pv(sV[buf], pb);
+        __syncthreads();
+      };
+      for (; i < n_lean; i += 2) {
+        half_lean(i, 0, 0);
+        half_lean(i + 1, 1, 1);
+      }
+    }
     for (; i + 1 < n; i += 2) {
       half(i, 0, 0);
       half(i + 1, 1, 1);
@@ -391,8 +444,9 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   }
 
   if (it.last) {
+    const float l_row = half_sum(l_run);   // the two lanes of the row, each its own keys
     if (!rvalid) return;
-    const float inv = 1.f / l_run;
+    const float inv = 1.f / l_row;
     T* orow = reinterpret_cast<T*>(a.out) + (((size_t)b * a.T + t) * a.Hq + g * G + hh) * DH;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

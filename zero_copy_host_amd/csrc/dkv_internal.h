@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dkv {
 
 constexpr int kMaxBatch = 256;   // sequences per call (lengths travel in kernel arguments)
@@ -17,6 +19,8 @@ constexpr int kWave = 64;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
 // ------------------------------------------------------------------ element traits
 // Each element type is moved in 16-byte vectors (VEC elements) and computed in fp32.
@@ -35,6 +39,11 @@ template <> struct Elem<__bf16> {
   }
   __device__ static inline __bf16 from_float(float f) { return static_cast<__bf16>(f); }
   __device__ static inline float to_float(__bf16 x) { return static_cast<float>(x); }
+  // acc + a + b in one dot2 instruction (fp32 accumulation)
+  __device__ static inline float dot2_ones(__bf16 a, __bf16 b, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a, b}, one, acc, false);
+  }
 };
 
 template <> struct Elem<_Float16> {
@@ -54,6 +63,10 @@ template <> struct Elem<_Float16> {
   }
   __device__ static inline _Float16 from_float(float f) { return static_cast<_Float16>(f); }
   __device__ static inline float to_float(_Float16 x) { return static_cast<float>(x); }
+  __device__ static inline float dot2_ones(_Float16 a, _Float16 b, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(f16x2{a, b}, one, acc, false);
+  }
 };
 
 template <> struct Elem<float> {
@@ -114,6 +127,18 @@ __device__ inline size_t host_row(const int32_t* table, int max_pages, int b, in
 }
 
 __device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// Lanes l and l + 32 hold the same query row in the transposed score layout: combine their
+// values with one lane-swap instruction (v_permlane32_swap: result[0] is x with its upper half
+// replaced by the lower half, result[1] x with its lower half replaced by the upper half).
+__device__ inline float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ------------------------------------------------------------------ launch arguments
 // Y = X·Wᵀ over up to three weight segments (Q, K, V) sharing one activation matrix.
