@@ -227,7 +227,7 @@ bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, i
 
 // ---- prefill workspace layout
 struct PrefillWs {
-  size_t q, k_new, v_new, state, total;
+  size_t q, k_new, v_new, state, nstate, total;
 };
 
 PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
@@ -238,7 +238,9 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   w.k_new = w.q + round_up((size_t)batch * T * n_q_heads * d * e, 256);
   w.v_new = w.k_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
   w.state = w.v_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
-  w.total = w.state + round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
+  const size_t sb = round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
+  w.nstate = w.state + sb;
+  w.total = w.nstate + sb;
   return w;
 }
 
@@ -269,16 +271,17 @@ int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged, int32_t q_til
   return (int)std::min<size_t>(keys, limit);
 }
 
-// Keys of [k0, k1) visible to the T new tokens of a sequence with past length L (token t
-// sees keys 0 .. L + t), summed over the tokens: the attention work of one super-chunk.
-long long visible_keys(int L, int T, int k0, int k1) {
-  auto sum_pos = [T](long long c) {   // sum over t in [0, T) of max(c + t, 0)
-    const long long t0 = std::max(0LL, 1 - c);
-    if (t0 >= T) return 0LL;
-    return (T - t0) * (2 * c + t0 + T - 1) / 2;
-  };
-  const long long c = (long long)L + 1 - k0;   // token t sees c + t keys of the range, unclamped
-  return sum_pos(c) - sum_pos(c - (k1 - k0));
+// Past-key items per pair dispatched ahead of a launch's own-key items: they bring the launch's
+// super-chunk over the host link into L2 while the own-key items compute, and compute at the
+// link's pace themselves (DIRECTKV_PREFILL_FETCHERS overrides it for tuning). 8B-shaped prefill,
+// one box: 0, 1, 2, 4, 8 fetchers per pair (per XCD) 5.19, 5.51, 5.50, 5.13, 5.10 ms; the
+// 70B-shaped prefill, link-hidden either way, 66.8-67.2 ms for all.
+int prefill_fetchers() {
+  if (const char* env = getenv("DIRECTKV_PREFILL_FETCHERS")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 0 && v <= 64) return (int)v;
+  }
+  return 8;
 }
 
 // block table of a paged cache, already copied into device memory (null: contiguous cache)
@@ -414,13 +417,16 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   void* kn = w + lay.k_new;
   void* vn = w + lay.v_new;
   float* state = reinterpret_cast<float*>(w + lay.state);
+  float* nstate = reinterpret_cast<float*>(w + lay.nstate);
 
   const bool separate = variant == DKV_PREFILL_SEPARATE;
+  const bool fused = variant == DKV_PREFILL_FUSED;
   ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
                           separate ? nullptr : vn);
-  // the fused path leaves the new rows in device memory here and writes the host copy from
-  // attention launches (below); the baselines write them from the GEMM
-  pa.host_out = variant != DKV_PREFILL_FUSED;
+  // The projection leaves the new rows in device memory, where attention reads them instead of
+  // fetching them back over the link; in the fused path the own-key items write their host copy
+  // (the storer role, beside their compute), the baselines write it from the projection epilogue.
+  pa.host_out = !fused;
   pa.table = pg.table;
   pa.max_pages = pg.max_pages;
   hipError_t e = fp(pa, s);
@@ -434,6 +440,7 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   aa.k_new = kn;
   aa.v_new = vn;
   aa.state = state;
+  aa.nstate = nstate;
   aa.out = out;
   aa.B = batch;
   aa.T = T;
@@ -443,90 +450,115 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   aa.table = pg.table;
   aa.max_pages = pg.max_pages;
   const int rows = attn_rows_per_tile();
-  aa.q_tiles = (T * G + rows - 1) / rows;
+  const int Q = (T * G + rows - 1) / rows;
+  aa.q_tiles = Q;
   const int P = batch * c->n_kv_heads;
   aa.xcd_group = variant != DKV_PREFILL_NAIVE && P >= 8 && xcd_placement();
   aa.new_from_host = separate;
+  aa.fetchers = prefill_fetchers();
+  aa.store_new = fused;
   for (int b = 0; b < batch; ++b) aa.past_len[b] = past_len[b];
   // With a multiple of 8 pairs, the pairs go in groups of 8, one pair per XCD: each XCD's L2
   // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which
   // halves the launches every query tile makes and the running-state traffic they cost.
   const int group = aa.xcd_group && P % 8 == 0 ? 8 : P;
+  auto launch = [&]() -> int {
+    const hipError_t le = fa(aa, s);
+    return le == hipSuccess ? DKV_OK : hip_fail(le, "attention launch");
+  };
   for (int pair0 = 0; pair0 < P; pair0 += group) {
     aa.pair0 = pair0;
     aa.pairs = group;
     const int b0 = pair0 / c->n_kv_heads, b1 = (pair0 + group - 1) / c->n_kv_heads;   // sequences served
-    // pairs of sequence b in this group
-    auto npairs = [&](int b) {
-      return std::min((b + 1) * c->n_kv_heads, pair0 + group) - std::max(b * c->n_kv_heads, pair0);
-    };
     int max_keys = 0, max_past = 0;
     for (int b = b0; b <= b1; ++b) {
       max_keys = std::max(max_keys, past_len[b] + T);
       max_past = std::max(max_past, past_len[b]);
     }
     // the naive baseline sweeps every key in one launch: no super-chunks, no XCD placement
-    const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged, aa.q_tiles);
-    // Key ranges of the launches: super-chunks of sk keys over the group's past keys, the last
-    // one ending at the longest past length. The keys after that are this step's rows; when
-    // they come from their device copies they need no L2 budget and go in one launch, which
-    // saves each query tile a running-state round trip per extra launch and lets the short
-    // tiles of the causal triangle run beside the long ones. (The separate-kernels baseline
-    // reads them from the host cache, so it keeps super-chunks over every key.)
-    std::vector<std::pair<int, int>> ranges;
-    int first_free = -1;
-    if (variant == DKV_PREFILL_NAIVE) {
-      ranges.emplace_back(0, max_keys);   // query-stationary: every key in one launch
-    } else if (separate) {
-      for (int k0 = 0; k0 < max_keys; k0 += sk) {
-        if (k0 >= max_past && first_free < 0) first_free = (int)ranges.size();
-        ranges.emplace_back(k0, std::min(k0 + sk, max_keys));
+    const int sk = variant == DKV_PREFILL_NAIVE ? std::max(max_keys, 1) : superchunk_keys(c, group, paged, Q);
+    if (!fused) {
+      // The baselines: launches over key ranges holding every key, past and new, each carrying the
+      // running state to the next (the separate-kernels baseline reads this step's rows back from
+      // the host cache, the naive one sweeps every key in one launch).
+      std::vector<std::pair<int, int>> ranges;
+      for (int k0 = 0; k0 < max_keys; k0 += sk) ranges.emplace_back(k0, std::min(k0 + sk, max_keys));
+      aa.past_items = 1;
+      aa.clip_past = 0;
+      aa.dev_q0 = aa.dev_q1 = 0;
+      aa.merge_new = aa.dev_final = 0;
+      for (size_t i = 0; i < ranges.size(); ++i) {
+        aa.kc0 = ranges[i].first;
+        aa.kc1 = ranges[i].second;
+        aa.first = i == 0;
+        aa.last = i + 1 == ranges.size();
+        int st = launch();
+        if (st) return st;
       }
-    } else {
-      // as many super-chunks as sk needs, of equal size (a multiple of 64 keys, at most sk), so
-      // that no launch sweeps a short remainder
-      const int n_host = (max_past + sk - 1) / sk;
-      const int skp = n_host > 0 ? std::min<int>(sk, (int)round_up((max_past + n_host - 1) / n_host, 64)) : sk;
-      for (int k0 = 0; k0 < max_past; k0 += skp) ranges.emplace_back(k0, std::min(k0 + skp, max_past));
-      first_free = (int)ranges.size();
-      ranges.emplace_back(max_past, max_keys);
+      continue;
     }
-    const int nl = (int)ranges.size();
-    // The new rows' host copies are written by launches whose keys hold no host rows (no
-    // past KV of any sequence in their range), so the writes cannot evict a resident
-    // super-chunk from L2; with no such launch, the last one writes them all. The rows are
-    // split among those launches in proportion to their attention work.
-    if (first_free < 0) first_free = nl - 1;
-    auto launch_work = [&](int i) {
-      long long wk_ = 0;
-      for (int b = b0; b <= b1; ++b)
-        wk_ += npairs(b) * visible_keys(past_len[b], T, ranges[i].first, ranges[i].second);
-      return wk_;
-    };
-    long long work_total = 0;
-    for (int i = first_free; i < nl; ++i) work_total += launch_work(i);
-    const long long new_rows = (long long)group * T;       // (pair, token) rows of this group
-    const long long row0 = (long long)pair0 * T;
-    long long work_before = 0;
-    for (int i = 0; i < nl; ++i) {
+    // The fused path. Past keys [0, past_len[b]) go in launches over super-chunks of equal size (a
+    // multiple of 64 keys, at most sk), the last ending at the longest past length, so no launch
+    // sweeps a short remainder. This step's own keys go as own-key items, one per query tile, each
+    // over all own keys its rows see, read from their device copies; they are spread over the
+    // past-key launches but the last (whose items fold their state in when they finalise), by
+    // equal shares of work, and each runs while its launch's fetcher items bring the super-chunk
+    // over the link. With one past-key launch they run in a launch of their own before it; with no
+    // past keys they are the only items and finalise the output themselves.
+    const int n_host = (max_past + sk - 1) / sk;
+    const int skp = n_host > 0 ? std::min<int>(sk, (int)round_up((max_past + n_host - 1) / n_host, 64)) : sk;
+    std::vector<std::pair<int, int>> ranges;
+    for (int k0 = 0; k0 < max_past; k0 += skp) ranges.emplace_back(k0, std::min(k0 + skp, max_past));
+    const int S = (int)ranges.size();
+    aa.clip_past = 1;
+    if (S <= 1) {
+      aa.past_items = 0;
+      aa.dev_q0 = 0;
+      aa.dev_q1 = Q;
+      aa.dev_final = S == 0;
+      aa.merge_new = 0;
+      aa.first = aa.last = 0;
+      int st = launch();
+      if (st || S == 0) {
+        if (st) return st;
+        continue;
+      }
+      aa.past_items = 1;
+      aa.dev_q0 = aa.dev_q1 = 0;
+      aa.dev_final = 0;
+      aa.kc0 = ranges[0].first;
+      aa.kc1 = ranges[0].second;
+      aa.first = aa.last = aa.merge_new = 1;
+      if ((st = launch())) return st;
+      continue;
+    }
+    // own-key work of query tile q: the rows' visible own keys, sum over rows of (row / G + 1)
+    std::vector<double> cum(Q + 1, 0.0);
+    for (int qt = 0; qt < Q; ++qt) {
+      const long long r0 = (long long)qt * rows, r1 = std::min<long long>((long long)T * G, r0 + rows) - 1;
+      double wq = 0.0;
+      for (long long t = r0 / G; t <= r1 / G; ++t)
+        wq += (double)(std::min<long long>(r1, (t + 1) * G - 1) - std::max<long long>(r0, t * G) + 1) * (double)(t + 1);
+      cum[qt + 1] = cum[qt] + wq;
+    }
+    int dq = 0;
+    for (int i = 0; i < S; ++i) {
       aa.kc0 = ranges[i].first;
       aa.kc1 = ranges[i].second;
       aa.first = i == 0;
-      aa.last = i == nl - 1;
-      aa.store_new = variant == DKV_PREFILL_FUSED && i >= first_free;
-      if (aa.store_new) {
-        const long long wl = launch_work(i);
-        if (work_total > 0) {
-          aa.store_lo = (int)(row0 + new_rows * work_before / work_total);
-          aa.store_hi = (int)(row0 + new_rows * (work_before + wl) / work_total);
-        } else {
-          aa.store_lo = (int)(row0 + new_rows * (i - first_free) / (nl - first_free));
-          aa.store_hi = (int)(row0 + new_rows * (i - first_free + 1) / (nl - first_free));
-        }
-        work_before += wl;
+      aa.last = aa.merge_new = i == S - 1;
+      aa.past_items = 1;
+      aa.dev_final = 0;
+      int dq1 = dq;
+      if (i < S - 1) {
+        const double goal = cum[Q] * (double)(i + 1) / (double)(S - 1);
+        while (dq1 < Q && (i == S - 2 || cum[dq1 + 1] <= goal + 1e-9)) ++dq1;
       }
-      e = fa(aa, s);
-      if (e != hipSuccess) return hip_fail(e, "attention launch");
+      aa.dev_q0 = dq;
+      aa.dev_q1 = dq1;
+      dq = dq1;
+      int st = launch();
+      if (st) return st;
     }
   }
   return DKV_OK;

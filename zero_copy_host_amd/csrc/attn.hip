@@ -80,35 +80,48 @@ struct AttnCfg {
 constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max past 2^8
 
 // One unit of prefill attention work: the query tile qt of (sequence, kv head) pair p against
-// the key super-chunk [kc0, kc1); `first` = no running state to read yet, `last` = finalise
-// the output after this super-chunk.
+// the keys [kc0, kc1), carrying its running softmax state in `state`; `first` = no state to read
+// yet, `last` = finalise the output after these keys, `merge` = at the finalisation, first merge
+// the state the item kept for this step's own keys (AttnArgs::nstate).
 struct AttnItem {
-  int p, qt, kc0, kc1, first, last;
+  int p, qt, kc0, kc1, first, last, merge;
+  float* state;
 };
 
-// Storer role: the (pair, token) rows [r0, r1) of this step's new K/V go from their device copy
-// to the host cache, 16 bytes per thread per step.
+// A 16-byte load of a key or value row piece; NT: non-temporal (the line is the first L2 evicts),
+// for own-key items that share a launch with past-key items, whose super-chunk must stay in L2.
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+template <bool NT>
+__device__ inline uint4 kv_load(const void* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
+// Storer role: the new K and V rows of tokens [t0, t1) of pair p go from their device copy to the
+// host cache rows [past_len[b] + t], 16 bytes per thread per step, with non-temporal stores.
 template <typename T, int DH, bool PAGED>
-__device__ inline void attn_store(const AttnArgs& a, const int r0, const int r1) {
-  using C = AttnCfg<T, DH>;
-  constexpr int CPR = DH / C::VEC;
-  for (int c = r0 * CPR + (int)threadIdx.x; c < r1 * CPR; c += C::THREADS) {
-    const int row = c / CPR, col = (c - row * CPR) * C::VEC;
-    const int pp = row / a.T, t = row - pp * a.T;
-    const int bb = pp / a.Hkv;
-    const size_t src = ((size_t)pp * a.T + t) * DH + col;
-    const size_t dst = host_row(PAGED ? a.table : nullptr, a.max_pages, bb, pp - bb * a.Hkv, a.Hkv, a.cap,
-                                a.past_len[bb] + t) * DH + col;
-    const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.k_new) + src);
-    const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.v_new) + src);
-    *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.kc)) + dst) = kv;
-    *reinterpret_cast<uint4*>(reinterpret_cast<T*>(const_cast<void*>(a.vc)) + dst) = vv;
+__device__ inline void attn_store(const AttnArgs& a, const int p, const int t0, const int t1) {
+  constexpr int VEC = 16 / (int)sizeof(T), CPR = DH / VEC;
+  const int b = p / a.Hkv, g = p - b * a.Hkv;
+  for (int c = t0 * CPR + (int)threadIdx.x; c < t1 * CPR; c += (int)blockDim.x) {
+    const int t = c / CPR, col = (c - t * CPR) * VEC;
+    const size_t src = ((size_t)p * a.T + t) * DH + col;
+    const size_t dst = host_row(PAGED ? a.table : nullptr, a.max_pages, b, g, a.Hkv, a.cap, a.past_len[b] + t) * DH + col;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.k_new) + src);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.v_new) + src);
+    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(reinterpret_cast<T*>(const_cast<void*>(a.kc)) + dst));
+    __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(reinterpret_cast<T*>(const_cast<void*>(a.vc)) + dst));
   }
 }
 
 // PAGED: the host cache is a page pool addressed through the block table; the page ids of
-// the item's host keys are staged in LDS before the sweep.
-template <typename T, int DH, int G, bool PAGED>
+// the item's host keys are staged in LDS before the sweep. NTKV: key/value loads are
+// non-temporal (own-key items beside past-key items in one launch).
+template <typename T, int DH, int G, bool PAGED, bool NTKV = false>
 __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& a, const AttnItem it) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
@@ -141,7 +154,8 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   const int qpos = L + t;
   const int nblk = (nrows + 31) >> 5;
   const bool wvalid = (row0 >> 5) + wave < nblk;   // this wave's 32-row block exists
-  float* st = a.state + ((size_t)p * nblk + (wvalid ? (row0 >> 5) + wave : 0)) * C::SBLK;
+  const size_t st_off = ((size_t)p * nblk + (wvalid ? (row0 >> 5) + wave : 0)) * C::SBLK;
+  float* st = it.state + st_off;
 
   f32x16 o[DB];
   float m_run = -INFINITY, l_run = 0.f;          // log2 domain, scaled scores
@@ -211,7 +225,7 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
         const int j = min(j0 + krow[i], key_hi - 1);
         const int e = off[i] - krow[i] * DH;
         const T* ks = j < host_end ? kh + hrow(j) : kn + (size_t)(j - L) * DH;
-        rk[set][i] = *reinterpret_cast<const uint4*>(ks + e);
+        rk[set][i] = kv_load<NTKV>(ks + e);
       }
     };
     auto gv = [&](int set, int j0) __attribute__((always_inline)) {
@@ -220,7 +234,7 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
         const int j = min(j0 + krow[i], key_hi - 1);
         const int e = off[i] - krow[i] * DH;
         const T* vs = j < host_end ? vh + hrow(j) : vn + (size_t)(j - L) * DH;
-        rv[set][i] = *reinterpret_cast<const uint4*>(vs + e);
+        rv[set][i] = kv_load<NTKV>(vs + e);
       }
     };
     auto sk = [&](int buf, int set, int j0) __attribute__((always_inline)) {
@@ -404,8 +418,8 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
         const T* vt = vsrc + (size_t)j0 * DH;
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
-          rk[set][u] = *reinterpret_cast<const uint4*>(kt + off[u]);
-          rv[set][u] = *reinterpret_cast<const uint4*>(vt + off[u]);
+          rk[set][u] = kv_load<NTKV>(kt + off[u]);
+          rv[set][u] = kv_load<NTKV>(vt + off[u]);
         }
       };
       auto sstore_lean = [&](int buf, int set) __attribute__((always_inline)) {
@@ -444,6 +458,25 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   }
 
   if (it.last) {
+    if (it.merge && wvalid) {
+      // fold in the state of this step's own keys: O = (o 2^(m - M) + o' 2^(m' - M)) / (l 2^(m - M) +
+      // l' 2^(m' - M)), M = max(m, m'); a sequence with no past keys has only the latter
+      const float* ns = a.nstate + st_off;
+      const float m2 = __builtin_nontemporal_load(ns + DB * 16 * 64 + lane);
+      const float l2 = __builtin_nontemporal_load(ns + (DB * 16 + 1) * 64 + lane);
+      const bool have_past = L > 0;
+      const float M = have_past ? fmaxf(m_run, m2) : m2;
+      const float a1 = have_past ? __builtin_amdgcn_exp2f(m_run - M) : 0.f;
+      const float a2 = __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float o2 = __builtin_nontemporal_load(ns + (db * 16 + v) * 64 + lane);
+          o[db][v] = have_past ? fmaf(o[db][v], a1, o2 * a2) : o2;
+        }
+      l_run = have_past ? fmaf(l_run, a1, l2 * a2) : l2;
+    }
     const float l_row = half_sum(l_run);   // the two lanes of the row, each its own keys
     if (!rvalid) return;
     const float inv = 1.f / l_row;
@@ -463,45 +496,63 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   }
 }
 
-// One launch per key super-chunk [a.kc0, a.kc1) of the pairs [a.pair0, a.pair0 + a.pairs).
+// One launch per key super-chunk [a.kc0, a.kc1) of the pairs [a.pair0, a.pair0 + a.pairs), carrying
+// a share of this step's own-key work: per pair, the items are taken in this order
+//   - a.fetchers past-key items (the heaviest query tiles), which bring the super-chunk over the
+//     host link into L2 while
+//   - the own-key items of query tiles [a.dev_q0, a.dev_q1) (this step's keys, read from their
+//     device copies: no host bytes, no L2 budget) keep the other CUs computing, then
+//   - the remaining past-key items, which find the super-chunk in L2.
+// No item waits for another: own-key items keep their own running state (a.nstate), which the
+// past-key items of the last launch fold in when they finalise (a.merge_new). With
+// a.past_items = 0 the launch holds own-key items only (a.dev_final: they finalise the output).
+// With at least 8 pairs, pair p is served only by XCD p % 8 (workgroup i runs on XCD i % 8).
 // The second bound is the minimum number of waves per SIMD; 16-bit types at d = 64 fit two
 // workgroups per CU (four waves per SIMD, at most 128 VGPRs a lane).
 template <typename T, int DH, int G, bool PAGED>
 __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
 void attn_kernel(const AttnArgs a) {
   const int P = a.pairs;
-  if (a.store_new) {
-    // storer role: this step's new K/V rows go from their device copy to the host cache.
-    // The host hands each storing launch a share of the (pair, token) rows, [store_lo,
-    // store_hi), split among the launches that hold no host rows (so the writes cannot evict
-    // a resident super-chunk from L2) in proportion to their attention work, so the writes
-    // drain under their compute. Every workgroup copies its part before any early exit.
-    const int per = (a.store_hi - a.store_lo + gridDim.x - 1) / gridDim.x;
-    const int r0 = a.store_lo + blockIdx.x * per, r1 = min(r0 + per, a.store_hi);
-    attn_store<T, DH, PAGED>(a, r0, r1);
-  }
-  // workgroup -> (sequence/kv-head pair p, query tile qt). With at least 8 pairs, pair p is
-  // served only by XCD p % 8 (workgroup i runs on XCD i % 8). Query tiles go out last row
-  // first: under the causal mask later rows see more keys, so the longest tiles start first.
-  int p, qt;
+  int p, r;   // pair, and the item's position in that pair's sequence of items
   if (a.xcd_group) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int ppx = (P + 7) >> 3;
     const int lp = (slot % ppx) * 8 + xcd;
-    qt = a.q_tiles - 1 - slot / ppx;
     if (lp >= P) return;
     p = a.pair0 + lp;
+    r = slot / ppx;
   } else {
     p = a.pair0 + blockIdx.x % P;
-    qt = a.q_tiles - 1 - blockIdx.x / P;
+    r = blockIdx.x / P;
   }
-  attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, a.kc1, a.first, a.last});
+  const int Q = a.q_tiles;
+  const int F = a.past_items ? min(a.fetchers, Q) : 0;
+  const int ND = a.dev_q1 - a.dev_q0;
+  const int L = a.past_len[p / a.Hkv];
+  // query tiles go out last row first: under the causal mask later rows see more keys
+  if (r >= F && r < F + ND) {
+    const int qt = a.dev_q1 - 1 - (r - F);
+    // the storer role: this item's query tile's tokens' new K/V rows go to the host cache (each
+    // query tile has exactly one own-key item, so every new row is written once)
+    if (a.store_new) {
+      constexpr int TPT = AttnCfg<T, DH>::ROWS / G;   // tokens per query tile
+      attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
+    }
+    const AttnItem it{p, qt, L, L + a.T, 1, a.dev_final, 0, a.nstate};
+    if (a.past_items) attn_item<T, DH, G, PAGED, true>(a, it);
+    else attn_item<T, DH, G, PAGED, false>(a, it);
+  } else {
+    const int qt = Q - 1 - (r < F ? r : r - ND);
+    const int kc1 = a.clip_past ? min(a.kc1, L) : a.kc1;
+    attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, kc1, a.first, a.last, a.merge_new, a.state});
+  }
 }
 
 template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int P = a.pairs;
-  const int grid = a.xcd_group ? 8 * ((P + 7) / 8) * a.q_tiles : P * a.q_tiles;
+  const int items = (a.past_items ? a.q_tiles : 0) + a.dev_q1 - a.dev_q0;   // per pair
+  const int grid = a.xcd_group ? 8 * ((P + 7) / 8) * items : P * items;
   hipLaunchKernelGGL((attn_kernel<T, DH, G, PAGED>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
   return hipGetLastError();
 }

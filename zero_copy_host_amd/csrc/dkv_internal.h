@@ -187,8 +187,9 @@ struct CombineArgs {
   int32_t split_begin[kMaxBatch + 1];
 };
 
-// Prefill attention over one super-chunk of keys [kc0, kc1) (absolute positions),
-// updating a per-row running softmax state in device memory.
+// Prefill attention over one super-chunk of keys [kc0, kc1) (absolute positions), updating a
+// per-row running softmax state in device memory, plus a share of the work over this step's own
+// keys (see attn_kernel).
 struct AttnArgs {
   const void* q;            // [B, T, Hq, d] device
   const void* kc;           // host cache (rows < past_len[b] are read from here)
@@ -196,6 +197,7 @@ struct AttnArgs {
   const void* k_new;        // [B, Hkv, T, d] device copy of this step's rows
   const void* v_new;
   float* state;             // running o, m, l (log2 domain) per 32 query rows: see attn_state_bytes
+  float* nstate;            // the same for this step's own keys (own-key items)
   void* out;                // [B, T, Hq*d]
   int32_t B, T, Hq, Hkv, cap;
   int32_t pair0, pairs;     // this launch serves (sequence, kv head) pairs [pair0, pair0 + pairs)
@@ -204,8 +206,13 @@ struct AttnArgs {
   int32_t q_tiles;          // row tiles per (b, g)
   int32_t xcd_group;        // 1: pair p is served only by XCD p % 8 (needs B*Hkv >= 8)
   int32_t new_from_host;    // 1: this step's rows are read back from the host cache too
-  int32_t store_new;        // 1: also copy this step's rows from k_new/v_new to the host cache
-  int32_t store_lo, store_hi;  // (pair, token) rows [store_lo, store_hi) this launch copies
+  int32_t past_items;       // 1: the launch holds the q_tiles past-key items of every pair
+  int32_t clip_past;        // 1: past-key items stop at past_len[b] (own keys are own-key items)
+  int32_t fetchers;         // past-key items per pair dispatched before the own-key items
+  int32_t dev_q0, dev_q1;   // own-key items of query tiles [dev_q0, dev_q1) per pair
+  int32_t dev_final;        // 1: own-key items finalise the output (no past keys anywhere)
+  int32_t merge_new;        // 1: finalising past-key items fold in nstate
+  int32_t store_new;        // 1: own-key items write their tokens' new rows to the host cache
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
   int32_t past_len[kMaxBatch];
