@@ -121,15 +121,26 @@ __device__ inline void attn_store(const AttnArgs& a, const int p, const int t0, 
 // PAGED: the host cache is a page pool addressed through the block table; the page ids of
 // the item's host keys are staged in LDS before the sweep. NTKV: key/value loads are
 // non-temporal (own-key items beside past-key items in one launch).
+// The workgroup's LDS: double-buffered key and value tiles and (paged caches) the page ids of a
+// launch's keys. Declared once in the kernel, so that every kind of item in it (each an
+// instantiation of attn_item) shares one allocation.
+template <typename T, int DH, bool PAGED>
+struct AttnLds {
+  T k[2][AttnCfg<T, DH>::KTILE];
+  T v[2][AttnCfg<T, DH>::VTILE];
+  int32_t pages[PAGED ? kPagedSuperchunk / kPageTokens + 1 : 1];
+};
+
 template <typename T, int DH, int G, bool PAGED, bool NTKV = false>
-__device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& a, const AttnItem it) {
+__device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& a, const AttnItem it,
+                                                                 AttnLds<T, DH, PAGED>& lds) {
   using C = AttnCfg<T, DH>;
   using MF = Mfma<T>;
   constexpr int KT = C::KT, VEC = C::VEC, LDK = C::LDK, LDV = C::LDV, LOADS = C::LOADS, DB = C::DB;
   constexpr int CPR = C::CPR, KPL = MF::KPL, KSTEP = MF::KSTEP;
-  __shared__ __attribute__((aligned(16))) T sK[2][C::KTILE];
-  __shared__ __attribute__((aligned(16))) T sV[2][C::VTILE];
-  __shared__ int32_t s_pages[PAGED ? kPagedSuperchunk / kPageTokens + 1 : 1];
+  auto& sK = lds.k;
+  auto& sV = lds.v;
+  auto& s_pages = lds.pages;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -507,11 +518,12 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
 // past-key items of the last launch fold in when they finalise (a.merge_new). With
 // a.past_items = 0 the launch holds own-key items only (a.dev_final: they finalise the output).
 // With at least 8 pairs, pair p is served only by XCD p % 8 (workgroup i runs on XCD i % 8).
-// The second bound is the minimum number of waves per SIMD; 16-bit types at d = 64 fit two
-// workgroups per CU (four waves per SIMD, at most 128 VGPRs a lane).
+// The second bound is the minimum number of waves per SIMD: two, 256 VGPRs a lane. (Four waves
+// per SIMD would leave 128, under what the three kinds of item need at d = 64.)
 template <typename T, int DH, int G, bool PAGED>
-__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, (DH == 64 && sizeof(T) == 2) ? 4 : DKV_ATTN_MINWAVES)
+__global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWAVES)
 void attn_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) AttnLds<T, DH, PAGED> lds;
   const int P = a.pairs;
   int p, r;   // pair, and the item's position in that pair's sequence of items
   if (a.xcd_group) {
@@ -539,12 +551,12 @@ void attn_kernel(const AttnArgs a) {
       attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
     }
     const AttnItem it{p, qt, L, L + a.T, 1, a.dev_final, 0, a.nstate};
-    if (a.past_items) attn_item<T, DH, G, PAGED, true>(a, it);
-    else attn_item<T, DH, G, PAGED, false>(a, it);
+    if (a.past_items) attn_item<T, DH, G, PAGED, true>(a, it, lds);
+    else attn_item<T, DH, G, PAGED, false>(a, it, lds);
   } else {
     const int qt = Q - 1 - (r < F ? r : r - ND);
     const int kc1 = a.clip_past ? min(a.kc1, L) : a.kc1;
-    attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, kc1, a.first, a.last, a.merge_new, a.state});
+    attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, kc1, a.first, a.last, a.merge_new, a.state}, lds);
   }
 }
 
