@@ -1,16 +1,21 @@
 """Benchmark of the host-KV attention layer on one MI355X.
 
-Default workload: a Llama-3-8B-shaped layer decode step in bf16 (D=4096, Hq=32, Hkv=8,
-d=128), batch 8, 32768 past tokens per sequence held in pinned host memory. A step is one
-attn_decode call: q/k/v projection of the new token, append of k/v to the host cache,
-split-KV attention over all 32769 keys, and the combine. Inputs are synthetic (seeded
-N(0,1) activations and past K/V, N(0, 1/D) weights) and resident before timing starts:
-X and W in device memory, the KV cache in pinned host memory, where the method keeps it.
+Headline workload: the Llama-3-70B-shaped layer in bf16 (D=8192, Hq=64, Hkv=8, d=128), batch 2:
+a chunked prefill of 16384 new tokens per sequence on 49152 past tokens held in pinned host
+memory (the cache then holds 65536 tokens), followed by 64 decode steps over that cache. A timed
+step is one attn_prefill call: the Q/K/V projection of the new tokens, their append to the host
+cache, and causal grouped-query attention over every past and new key; the value is prefill
+tokens per second (B*T / step time), and the 64 decode steps after it are reported beside it in
+microseconds per step. Inputs are synthetic (seeded N(0,1) activations and past K/V, N(0, 1/D)
+weights) and resident before timing starts: X and W in device memory, the KV cache in pinned host
+memory, where the method keeps it.
 
-Prints one JSON line. Extra objects: the measured host-link peak (kernel streaming
-read/write of pinned memory), the roofline of the decode kernel, the oracle timed on the
-host cores (cpu_baseline), and a chunked-prefill measurement (8192 new tokens on 24576
-host-resident past tokens) for the prefill half of the metric.
+Prints one JSON line. Extra objects: the measured host-link peak (kernel streaming read/write of
+pinned memory), the roofline of the dominant kernel (prefill attention: its duration from HIP
+events on the library's stream, its algorithmic flops per launch), the oracle timed on the host
+cores over a bounded sample (cpu_baseline), and every other named workload (8B-shaped decode and
+chunked prefill, fp16 long-context decode, the tiny fp32 layer, ablations, paged cache, staging
+baseline, decoder stack) each with its own roofline.
 """
 from __future__ import annotations
 
@@ -29,7 +34,6 @@ sys.path.insert(0, ROOT)
 PCIE5_X16_GBPS = 63.0      # published PCIe 5.0 x16 rate per direction (32 GT/s, 128b/130b)
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense
-PROFILE_NOTE = os.path.join(ROOT, "profiles", "decode_llama8b_b8_L32768_counters.txt")
 
 
 def log(msg):
@@ -86,54 +90,95 @@ def hostlink_peak(dkv, nbytes=1 << 30, reps=8):
     return res
 
 
-def setup_decode(dkv, w, seed_off=0):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads():
+    import threadpoolctl
+    return max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+
+
+def cpu_baseline_prefill(name, n_tokens=128):
+    """The oracle, as it is, on a bounded sample of workload `name`'s prefill step: the first
+    n_tokens of the step's new tokens (every sequence, every head), on the same past keys. Its
+    rate is the sample's tokens over the oracle's time; later tokens of the full step see up to
+    T more keys, so the full step would run slower per token."""
+    import oracle
     import synth
-    dr = synth.Draw(w.seed + seed_off)
+    w = synth.workload(name)
+    dr = synth.Draw(w.seed)
+    wq, wk, wv = synth.layer_weights(dr, w.D, w.Hq, w.Hkv, w.d, w.dtype)
+    past = np.asarray(w.past, dtype=np.int32) if w.past is not None else dr.lengths(w.B, w.past_lo, w.past_hi)
+    x = dr.normal((w.B, w.T, w.D), 1.0, w.dtype)[:, :n_tokens]
+    cap = int(max(past)) + n_tokens
+    kc = np.zeros((w.B, w.Hkv, cap, w.d), dtype=np.float32)
+    vc = np.zeros_like(kc)
+    synth.fill_past(dr, kc, vc, past, w.dtype)
+    t0 = time.perf_counter()
+    oracle.layer_step(x, wq, wk, wv, kc, vc, past, w.Hq, w.dtype)
+    el = time.perf_counter() - t0
+    tok = w.B * n_tokens
+    return {"value": tok / el, "unit": "prefill tok/s per layer", "cores": int(_oracle_threads()), "kind": "oracle",
+            "seconds": el, "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"the first {n_tokens} of the {w.T} new tokens of each of the {w.B} sequences of {name} "
+                      f"(projection, append, causal attention over {int(past[0])}+ keys, all {w.Hq} heads), "
+                      f"numpy fp64 oracle; the full step's later tokens see up to {w.T} more keys each"}
+
+
+def cpu_baseline_decode(name, min_seconds=10.0):
+    """The oracle, as it is, on whole decode steps of workload `name`, repeated for ~min_seconds."""
+    import oracle
+    import synth
+    w = synth.workload(name)
+    dr = synth.Draw(w.seed)
     wq, wk, wv = synth.layer_weights(dr, w.D, w.Hq, w.Hkv, w.d, w.dtype)
     past = np.asarray(w.past, dtype=np.int32) if w.past is not None else dr.lengths(w.B, w.past_lo, w.past_hi)
     x = dr.normal((w.B, 1, w.D), 1.0, w.dtype)
-    cache = dkv.HostKVCache(w.B, w.Hkv, w.d, w.cap, w.dtype)
-    synth.fill_past(dr, cache.k, cache.v, past, w.dtype)
-    return dict(wq=wq, wk=wk, wv=wv, x=x, past=past, cache=cache)
-
-
-def cpu_baseline_decode(w, s, min_seconds=10.0):
-    """The oracle, as it is, on the same decode step, repeated for ~min_seconds."""
-    import oracle
-    import synth
-    import threadpoolctl
-    kc = synth.from_storage(s["cache"].k, w.dtype)
-    vc = synth.from_storage(s["cache"].v, w.dtype)
+    kc = np.zeros((w.B, w.Hkv, w.cap, w.d), dtype=np.float32)
+    vc = np.zeros_like(kc)
+    synth.fill_past(dr, kc, vc, past, w.dtype)
     t0 = time.perf_counter()
     n = 0
     while True:
-        oracle.layer_step(s["x"], s["wq"], s["wk"], s["wv"], kc, vc, s["past"], w.Hq, w.dtype)
+        oracle.layer_step(x, wq, wk, wv, kc, vc, past, w.Hq, w.dtype)
         n += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": el / n * 1e6, "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} full decode step(s) of the same workload (all {w.B} sequences, "
-                      f"{int(s['past'][0]) + 1} keys each) in fp64 numpy; host has {os.cpu_count()} cpus"}
+    return {"value": el / n * 1e6, "unit": "us per layer decode step", "cores": int(_oracle_threads()),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{n} full decode step(s) of {name} (all {w.B} sequences, {int(past[0]) + 1} keys each), "
+                      f"numpy fp64 oracle"}
 
 
-def profile_traffic(kernel_src_hash):
-    """HBM/host bytes per decode launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
-    if not os.path.exists(PROFILE_NOTE):
-        return None, None
+def read_counter_summary(name, kernel_src_hash):
+    """Key/value lines of profiles/<name>_counters.txt if it was taken on the current kernel
+    source (its kernel_source_sha1 line), else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.txt")
+    if not os.path.exists(path):
+        return None
     vals = {}
-    for line in open(PROFILE_NOTE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha1") != kernel_src_hash:
-        return None, None
+        return None
+    return vals
+
+
+def _float(vals, key):
     try:
-        return float(vals["fetch_plus_write_bytes_per_launch"]), float(vals["host_read_bytes_per_launch"])
+        return float(vals[key]) if vals else None
     except (KeyError, ValueError):
-        return None, None
+        return None
 
 
 def src_hash(*names):
@@ -202,10 +247,65 @@ def _decode_stats(w, past, ms, peak_read):
             "overlap_model": _overlap_model(1, past, host_read, flops, MFMA_PEAK_TFLOPS[w.dtype], ms, peak_read)}
 
 
+ATTN_SRC = ("attn.hip", "dkv_internal.h")
+DECODE_SRC = ("decode.hip", "dkv_internal.h")
+
+
+def _phase(t, name, steps):
+    ms, n = t[name]
+    if not n:
+        return None
+    return {"ms_per_step": ms / steps, "launches_per_step": n / steps, "avg_launch_ms": ms / n}
+
+
+def _prefill_roofline(w, past, kern, name):
+    """Prefill attention against the dtype's dense matrix-core peak: algorithmic attention flops
+    per launch (the step's 4*d*Hq*sum_b(T*L_b + T(T+1)/2), spread over its launches) over the
+    launches' mean duration (HIP events on the library's stream)."""
+    from zero_copy_host_amd import accounting as acc
+    a = kern.get("prefill_attention") if kern else None
+    if not a:
+        return None
+    flops = acc.attention_flops(past, w.T, w.Hq, w.d)
+    per_launch = flops / a["launches_per_step"]
+    achieved = per_launch / (a["avg_launch_ms"] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    ctr = read_counter_summary(name, src_hash(*ATTN_SRC))
+    return {"bound": "mfma", "kernel": "attn_kernel (prefill attention; every launch of a step)",
+            "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "algorithmic_flops_per_launch": per_launch, "launches_per_step": a["launches_per_step"],
+            "avg_launch_ms": a["avg_launch_ms"], "traffic": _float(ctr, "attn_fetch_plus_write_bytes_per_launch"),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
+            "host_read_bytes_per_step_measured": _float(ctr, "host_read_bytes_per_step")}
+
+
+def _decode_roofline(w, past, kern, peak_read, name):
+    """The decode attention kernel against the host link: algorithmic host bytes per launch (every
+    past K and V row once, 2*Hkv*d*e*sum_b L_b) over its mean duration (HIP events)."""
+    import synth
+    from zero_copy_host_amd import accounting as acc
+    a = kern.get("decode_attention") if kern else None
+    if not a:
+        return None
+    e = synth.elem_bytes(w.dtype)
+    read = acc.host_read_bytes(past, w.Hkv, w.d, e)
+    achieved = read / (a["avg_launch_ms"] * 1e-3) / 1e9
+    ctr = read_counter_summary(name, src_hash(*DECODE_SRC))
+    return {"bound": "host_link", "kernel": "decode_kernel", "achieved": achieved, "peak": PCIE5_X16_GBPS,
+            "unit": "GB/s", "frac": achieved / PCIE5_X16_GBPS,
+            "peak_note": "PCIe 5.0 x16 per direction; the measured kernel read peak is beside it",
+            "measured_read_peak": peak_read, "frac_of_measured_read_peak": achieved / peak_read if peak_read else None,
+            "algorithmic_bytes_per_launch": read + acc.host_write_bytes(w.B, 1, w.Hkv, w.d, e),
+            "avg_launch_ms": a["avg_launch_ms"], "traffic": _float(ctr, "fetch_plus_write_bytes_per_launch"),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
+            "host_read_bytes_measured": _float(ctr, "host_read_bytes_per_launch")}
+
+
 def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, variant="fused",
                 ablations=()):
     """Time the prefill step of workload `name` (fixed past lengths, so every step rewrites the
-    same rows); optionally follow it with real decode steps at advancing lengths."""
+    same rows), with the library's kernel timing on; optionally follow it with real decode steps
+    at advancing lengths."""
     import torch
     import synth
     w = synth.workload(name)
@@ -213,17 +313,26 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
     out = torch.empty((w.B, w.T, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
     ws = torch.empty(dkv.workspace_bytes("prefill_staged" if variant == "staged" else "prefill", cache, w.B, w.T, w.Hq),
                      dtype=torch.uint8, device="cuda")
-    def timed(var, n, nwarm):
+
+    def timed(var, n, nwarm, kernels=False):
         for _ in range(nwarm):
             dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
         torch.cuda.synchronize()
+        if kernels:
+            dkv.timing(True)
         with EventTimer() as t:
             for _ in range(n):
                 dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
-        return t.ms / n
+        kern = None
+        if kernels:
+            tr = dkv.timing_read()
+            dkv.timing(False)
+            kern = {ph: _phase(tr, ph, n) for ph in ("projection", "prefill_attention")}
+        return t.ms / n, kern
 
-    res = {"workload": name, "steps": steps, "variant": variant,
-           **_prefill_stats(w, past, timed(variant, steps, warmup), peak_read)}
+    ms, kern = timed(variant, steps, warmup, kernels=True)
+    res = {"workload": name, "steps": steps, "variant": variant, **_prefill_stats(w, past, ms, peak_read),
+           "kernels": kern, "roofline": _prefill_roofline(w, past, kern, name) if variant == "fused" else None}
     if ablations:
         # the baselines the pages compare the method against, on the same inputs
         res["ablations_ms"] = {}
@@ -235,7 +344,7 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
                 ws = torch.empty(dkv.workspace_bytes("prefill_staged", cache, w.B, w.T, w.Hq), dtype=torch.uint8,
                                  device="cuda")
                 res["device_workspace_bytes"][v] = ws.numel()
-            res["ablations_ms"][v] = timed(v, 2, 1)
+            res["ablations_ms"][v] = timed(v, 2, 1)[0]
     if decode_steps:
         del out, ws
         xs = [to_dev(dr.normal((w.B, 1, w.D), 1.0, w.dtype), w.dtype) for _ in range(decode_steps)]
@@ -247,20 +356,27 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
         # a single decode step is timed as the mean of 20 runs of that step (same lengths, so
         # each run rewrites the same row); longer runs advance the lengths step by step
         reps = 20 if decode_steps == 1 else 1
+        dkv.timing(True)
         with EventTimer() as t:
             for _ in range(reps):
                 for s_ in range(decode_steps):
                     dkv.attn_decode(cache, xs[s_], dev["wq"], dev["wk"], dev["wv"], past + w.T + s_, w.Hq, outd, wsd)
-        ms = t.ms / (decode_steps * reps)
+        tr = dkv.timing_read()
+        dkv.timing(False)
+        n = decode_steps * reps
+        ms = t.ms / n
         mid = past + w.T + decode_steps // 2
-        res["decode"] = {"steps": decode_steps, "timed_runs": decode_steps * reps, "past_len_first": int(past[0] + w.T),
-                         **_decode_stats(w, mid, ms, peak_read)}
+        kd = {ph: _phase(tr, ph, n) for ph in ("decode_qproj", "decode_attention", "decode_combine")}
+        res["decode"] = {"steps": decode_steps, "timed_runs": n, "past_len_first": int(past[0] + w.T),
+                         **_decode_stats(w, mid, ms, peak_read), "kernels": kd,
+                         "roofline": _decode_roofline(w, mid, kd, peak_read, name + "_decode")}
     cache.free()
     return res
 
 
 def run_decode(dkv, name, steps=10, warmup=2, peak_read=None):
-    """Time a decode step of workload `name` at fixed past lengths."""
+    """Time a decode step of workload `name` at fixed past lengths (every step rewrites the same
+    new row), with the library's kernel timing on."""
     import torch
     import synth
     w = synth.workload(name)
@@ -270,12 +386,17 @@ def run_decode(dkv, name, steps=10, warmup=2, peak_read=None):
     for _ in range(warmup):
         dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
     torch.cuda.synchronize()
+    dkv.timing(True)
     with EventTimer() as t:
         for _ in range(steps):
             dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
+    tr = dkv.timing_read()
+    dkv.timing(False)
     cache.free()
+    kd = {ph: _phase(tr, ph, steps) for ph in ("decode_qproj", "decode_attention", "decode_combine")}
     return {"workload": name, "steps": steps, "past_len": [int(x) for x in past],
-            **_decode_stats(w, past, t.ms / steps, peak_read)}
+            **_decode_stats(w, past, t.ms / steps, peak_read), "kernels": kd,
+            "roofline": _decode_roofline(w, past, kd, peak_read, name)}
 
 
 def _paged_copy(dkv, w, past, cache, seed):
@@ -428,10 +549,6 @@ def run_stack(dkv, name, tokens=3, peak_read=None):
     return res
 
 
-def bench_prefill(dkv, steps=5, warmup=2):
-    return run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps, warmup)
-
-
 def calibration_kernels(dkv, nbytes=1 << 30):
     """Kernels of known traffic for scaling the memory counters: one streaming read and one
     streaming write of nbytes of pinned host memory, and one device-to-device copy of
@@ -450,22 +567,52 @@ def calibration_kernels(dkv, nbytes=1 << 30):
     print(json.dumps({"calibration_bytes": nbytes}), flush=True)
 
 
+def counters_summary(paths):
+    """Per-kernel mean of every counter per dispatch over rocprofv3 --pmc CSV files, printed as
+    JSON (the figures the counter summaries under profiles/ quote)."""
+    import collections
+    import csv
+    out = {}
+    for path in paths:
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        disp = collections.defaultdict(set)
+        for r in csv.DictReader(open(path)):
+            k = r["Kernel_Name"].split("(")[0]
+            agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[k].add(r["Dispatch_Id"])
+        for k, cs in agg.items():
+            n = len(disp[k])
+            out.setdefault(k, {"dispatches": 0})
+            out[k]["dispatches"] = max(out[k]["dispatches"], n)
+            out[k].update({c: v / n for c, v in cs.items()})
+    print(json.dumps(out, indent=1), flush=True)
+
+
+HEADLINE = "llama70b_prefill_T16384_on_L49152_b2_bf16"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_decode_b8_L32768_bf16")
+    ap.add_argument("--steps", type=int, default=5, help="timed prefill steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="the headline workload only")
     ap.add_argument("--variant", default="fused", choices=["fused", "naive", "separate", "staged"],
                     help="prefill variant for --profile prefill (the ablation baselines)")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode", choices=["decode", "prefill", "paged", "staging", "stack", "calib"],
-                    help="short run for rocprofv3: decode steps only, prefill steps only, the paged-cache "
-                         "decode and prefill, the staging baseline, the 8B/70B decoder stacks, or the "
-                         "counter calibration kernels (1 GiB host read, 1 GiB host write, 1 GiB "
-                         "device-to-device copy)")
+    ap.add_argument("--profile", nargs="?", const="prefill",
+                    choices=["decode", "prefill", "paged", "staging", "stack", "calib"],
+                    help="short run for rocprofv3: prefill steps of --workload (default the headline), decode "
+                         "steps of --workload (a decode workload), the paged-cache decode and prefill, the "
+                         "staging baseline, the 8B/70B decoder stacks, or the counter calibration kernels "
+                         "(1 GiB host read, 1 GiB host write, 1 GiB device-to-device copy)")
+    ap.add_argument("--counters-summary", nargs="+", metavar="CSV",
+                    help="print per-kernel per-dispatch means of rocprofv3 --pmc CSV files and exit")
     args = ap.parse_args()
+    if args.counters_summary:
+        counters_summary(args.counters_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the host-KV layer path runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
@@ -497,105 +644,69 @@ def main():
               flush=True)
         return
     if args.profile == "prefill":
-        # the 8B chunked prefill unless --workload names another prefill workload
-        name = args.workload if synth.workload(args.workload).T > 1 else "llama8b_prefill_T8192_on_L24576_bf16"
+        name = args.workload if synth.workload(args.workload).T > 1 else HEADLINE
         print(json.dumps({"prefill": run_prefill(dkv, name, steps=args.steps,
                                                  warmup=args.warmup, variant=args.variant)}), flush=True)
         return
-    if args.profile:
-        args.no_cpu_baseline = args.no_prefill = True
+    if args.profile == "decode":
+        name = args.workload if synth.workload(args.workload).T == 1 else "llama8b_decode_b8_L32768_bf16"
+        print(json.dumps({"decode": run_decode(dkv, name, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
 
-    peak = {"read": None, "write": None}
-    if not args.profile:
-        log("measuring host-link peak")
-        peak = hostlink_peak(dkv)
-
+    log("measuring host-link peak")
+    peak = hostlink_peak(dkv)
+    pr = peak["read"]
     w = synth.workload(args.workload)
-    assert w.T == 1, "the timed workload is a decode step"
-    log(f"setting up {w.name}")
-    s = setup_decode(dkv, w)
-    xd = to_dev(s["x"], w.dtype)
-    wqd, wkd, wvd = to_dev(s["wq"].T, w.dtype), to_dev(s["wk"].T, w.dtype), to_dev(s["wv"].T, w.dtype)
-    out = torch.empty((w.B, 1, w.Hq * w.d), dtype=tdtype(w.dtype), device="cuda")
-    ws = torch.empty(dkv.workspace_bytes("decode", s["cache"], w.B, 1, w.Hq), dtype=torch.uint8, device="cuda")
-    past = s["past"]
-
-    def step():
-        # fixed lengths: every step rewrites the same new-token row
-        dkv.attn_decode(s["cache"], xd, wqd, wkd, wvd, past, w.Hq, out, ws)
-
-    log(f"warmup {args.warmup}, timing {args.steps} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    with EventTimer() as t:
-        for _ in range(args.steps):
-            step()
-    ms = t.ms / args.steps
-    torch.cuda.synchronize()
-
-    from zero_copy_host_amd import accounting as acc
-    e = synth.elem_bytes(w.dtype)
-    host_read = acc.host_read_bytes(past, w.Hkv, w.d, e)         # every past row, K and V, once
-    host_write = acc.host_write_bytes(w.B, 1, w.Hkv, w.d, e)     # the new row
-    achieved = host_read / (ms * 1e-3) / 1e9
-    traffic, host_meas = profile_traffic(src_hash("decode.hip", "dkv_internal.h"))
+    assert w.T > 1, "the headline workload is a prefill step"
+    log(f"{w.name}: {args.warmup} warmup and {args.steps} timed prefill steps, then {w.decode_steps} decode steps")
+    head = run_prefill(dkv, w.name, steps=args.steps, warmup=args.warmup, peak_read=pr, decode_steps=w.decode_steps)
+    ms = head["ms_per_step"]
     result = {
         "metric": "prefill tok/s & decode step us per layer; host-link GB/s vs measured peak",
-        "value": ms * 1e3,
-        "unit": "us per layer decode step",
+        "value": head["tok_per_s"],
+        "unit": "prefill tok/s per layer (B*T new tokens / step time)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) X and past K/V, N(0,1/D) weights)",
-        "config": {"workload": w.name, "batch": w.B, "past_len": int(past[0]), "new_tokens": 1,
-                   "D": w.D, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "kv_cache": "pinned host memory"},
-        "decode_tok_per_s": w.B / (ms * 1e-3),
-        "overlap_model": _overlap_model(
-            1, past, host_read, acc.attention_flops(past, 1, w.Hq, w.d) + acc.projection_flops(w.B, 1, w.D, w.Hq, w.Hkv, w.d),
-            MFMA_PEAK_TFLOPS[w.dtype], ms, peak["read"]),
-        "roofline": {"bound": "host_link", "kernel": "decode_kernel (+ qproj_kernel, combine_kernel) per attn_decode call",
-                     "achieved": achieved, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                     "frac": achieved / PCIE5_X16_GBPS,
-                     "peak_note": "PCIe 5.0 x16 per direction; measured kernel read peak below",
-                     "measured_read_peak": peak["read"],
-                     "frac_of_measured_read_peak": (achieved / peak["read"]) if peak["read"] else None,
-                     "algorithmic_bytes_per_launch": host_read + host_write,
-                     "traffic": traffic, "host_read_bytes_measured": host_meas},
+        "config": {"workload": w.name, "batch": w.B, "new_tokens": w.T, "past_len": int(w.past[0]),
+                   "decode_steps_after": w.decode_steps, "D": w.D, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d,
+                   "kv_cache": "pinned host memory"},
+        "roofline": head["roofline"],
+        "prefill": {k: v for k, v in head.items() if k not in ("roofline", "decode")},
+        "decode": head.get("decode"),
         "host_link": {"kernel_read_GBps": peak["read"], "kernel_write_GBps": peak["write"]},
     }
-    if not args.no_prefill:
-        pr = peak["read"]
-        log("other workloads: tiny fp32 layer")
-        tiny = run_prefill(dkv, "tiny_f32_prefill128_decode1", steps=20, warmup=3, peak_read=pr, decode_steps=1)
-        log("8B chunked prefill")
-        result["prefill"] = run_prefill(dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=5, warmup=2, peak_read=pr,
-                                        ablations=("naive", "separate", "staged"))
+    if not args.no_others:
+        others = {}
+        log("8B-shaped decode, B=8, L=32768")
+        others["llama8b_decode_b8_L32768_bf16"] = run_decode(dkv, "llama8b_decode_b8_L32768_bf16", steps=20,
+                                                              warmup=3, peak_read=pr)
+        log("8B-shaped chunked prefill and its ablations")
+        others["llama8b_prefill_T8192_on_L24576_bf16"] = run_prefill(
+            dkv, "llama8b_prefill_T8192_on_L24576_bf16", steps=5, warmup=2, peak_read=pr,
+            ablations=("naive", "separate", "staged"))
+        log("long-context fp16 decode")
+        others["long_decode_b4_L96k_128k_f16"] = run_decode(dkv, "long_decode_b4_L96k_128k_f16", steps=6, warmup=1,
+                                                             peak_read=pr)
+        log("tiny fp32 layer")
+        others["tiny_f32_prefill128_decode1"] = run_prefill(dkv, "tiny_f32_prefill128_decode1", steps=20, warmup=3,
+                                                            peak_read=pr, decode_steps=1)
+        log("70B-shaped prefill from an empty cache + 64 decode steps (the other reading of that case)")
+        others["llama70b_prefill_T16384_empty_b2_bf16"] = run_prefill(
+            dkv, "llama70b_prefill_T16384_empty_b2_bf16", steps=2, warmup=1, peak_read=pr, decode_steps=64)
+        log("paged host cache: 8B decode and 8B chunked prefill")
+        result["paged"] = run_paged(dkv, peak_read=pr)
         log("staging baseline: 8B decode")
         result["staging_baseline"] = run_staging(dkv, peak_read=pr)
         log("decoder stack: 32 layers of the 8B layer, per-token latency")
         result["decode_stack"] = {"llama8b_32layers_b8_L32768": run_stack(dkv, "llama8b_32layers_b8_L32768",
                                                                           tokens=2, peak_read=pr)}
-        log("long-context fp16 decode")
-        longd = run_decode(dkv, "long_decode_b4_L96k_128k_f16", steps=6, warmup=1, peak_read=pr)
-        log("70B prefill + 64 decode steps")
-        big = run_prefill(dkv, "llama70b_prefill_T16384_on_L49152_b2_bf16", steps=2, warmup=1, peak_read=pr,
-                          decode_steps=64)
-        log("70B prefill from an empty cache + 64 decode steps (the other reading of that case)")
-        big0 = run_prefill(dkv, "llama70b_prefill_T16384_empty_b2_bf16", steps=2, warmup=1, peak_read=pr,
-                           decode_steps=64)
-        log("paged host cache: 8B decode and 8B chunked prefill")
-        result["paged"] = run_paged(dkv, peak_read=pr)
-        result["workloads"] = {"tiny_f32_prefill128_decode1": tiny,
-                               "llama8b_prefill_T8192_on_L24576_bf16": result["prefill"],
-                               "long_decode_b4_L96k_128k_f16": longd,
-                               "llama70b_prefill_T16384_on_L49152_b2_bf16": big,
-                               "llama70b_prefill_T16384_empty_b2_bf16": big0}
+        result["workloads"] = others
     if not args.no_cpu_baseline:
-        # after every GPU measurement: the oracle's threads on all host cores would otherwise
-        # slow the kernel launches of the launch-bound workloads measured after it
+        # after every GPU measurement: the oracle's threads on the host cores would otherwise slow
+        # the kernel launches of the launch-bound workloads
         log("timing the oracle on the host cores")
-        result["cpu_baseline"] = cpu_baseline_decode(w, s)
-    s["cache"].free()
+        result["cpu_baseline"] = cpu_baseline_prefill(w.name)
     print(json.dumps(result), flush=True)
 
 

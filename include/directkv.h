@@ -306,6 +306,20 @@ int dkv_swiglu(const void* gate_up, void* y, int32_t rows, int32_t F, int32_t dt
  */
 int dkv_hostlink_stream(void* host_ptr, size_t bytes, int32_t mode, int32_t n_wg, void* stream);
 
+/*
+ * Kernel timing for measurement ([N] Experiments & Results report per-kernel latency): with
+ * dkv_timing(1) every later layer call also records HIP events on its own stream around each of
+ * its kernel phases; dkv_timing(0) stops (both calls drop what was recorded). dkv_timing_read
+ * waits for the recorded events and returns, per phase, the summed elapsed milliseconds and the
+ * number of kernel launches they cover, in ms[i] and launches[i] for i < n:
+ *   0 projection GEMM (prefill, append), 1 prefill attention (all launches of each call),
+ *   2 decode query projection, 3 decode attention, 4 decode combine.
+ * Timing adds two events per phase per call; it does not change results. Errors: INVALID_ARG
+ * (null output, n <= 0), HIP (an event failed).
+ */
+int dkv_timing(int32_t enable);
+int dkv_timing_read(float* ms, int32_t* launches, int32_t n);
+
 /* Thread-local text describing the last non-zero status returned on this thread. */
 const char* dkv_last_error(void);
 

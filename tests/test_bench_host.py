@@ -55,3 +55,52 @@ def test_prefill_and_decode_statistics_of_the_8b_workloads():
     assert sd["host_read_bytes"] == 1 << 30
     assert sd["host_read_GBps"] == pytest.approx((1 << 30) / 19.3e-3 / 1e9)
     assert sd["frac_of_measured_read_peak"] == pytest.approx(sd["host_read_GBps"] / 55.8)
+
+
+def test_prefill_roofline_from_kernel_timing():
+    """achieved = the step's algorithmic attention flops per launch over the launches' mean
+    duration; the 70B-shaped step is 2 x 4 * 128 * 64 * (16384 * 49152 + 16384 * 16385 / 2) flops."""
+    w = synth.workload("llama70b_prefill_T16384_on_L49152_b2_bf16")
+    past = np.asarray(w.past, dtype=np.int32)
+    kern = {"prefill_attention": {"ms_per_step": 60.0, "launches_per_step": 32.0, "avg_launch_ms": 1.875}}
+    r = bench._prefill_roofline(w, past, kern, "no_such_profile")
+    flops = 2 * 4 * 128 * 64 * (16384 * 49152 + 16384 * 16385 / 2)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert r["algorithmic_flops_per_launch"] == pytest.approx(flops / 32)
+    assert r["achieved"] == pytest.approx(flops / 60e-3 / 1e12)
+    assert r["frac"] == pytest.approx(r["achieved"] / 2500.0)
+    assert r["traffic"] is None                              # no counter summary for this name
+    assert bench._prefill_roofline(w, past, {"prefill_attention": None}, "x") is None
+
+
+def test_decode_roofline_from_kernel_timing():
+    w = synth.workload("llama8b_decode_b8_L32768_bf16")
+    past = np.asarray(w.past, dtype=np.int32)
+    kern = {"decode_attention": {"ms_per_step": 19.2, "launches_per_step": 1.0, "avg_launch_ms": 19.2}}
+    r = bench._decode_roofline(w, past, kern, 56.0, "no_such_profile")
+    assert r["bound"] == "host_link" and r["unit"] == "GB/s"
+    assert r["achieved"] == pytest.approx((1 << 30) / 19.2e-3 / 1e9)
+    assert r["frac_of_measured_read_peak"] == pytest.approx(r["achieved"] / 56.0)
+    assert r["algorithmic_bytes_per_launch"] == (1 << 30) + 8 * 8 * 2 * 256
+
+
+def test_counter_summary_is_gated_on_the_kernel_source(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "wl_counters.txt").write_text("# comment\nkernel_source_sha1: abc\nattn_fetch_plus_write_bytes_per_launch: 1.5e9\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.read_counter_summary("wl", "abc")["attn_fetch_plus_write_bytes_per_launch"] == "1.5e9"
+    assert bench.read_counter_summary("wl", "def") is None
+    assert bench.read_counter_summary("other", "abc") is None
+
+
+def test_counters_summary_means_per_dispatch(tmp_path, capsys):
+    f = tmp_path / "c.csv"
+    f.write_text("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+                 "1,kA(int),FETCH_SIZE,10\n1,kA(int),FETCH_SIZE,20\n2,kA(int),FETCH_SIZE,30\n"
+                 "3,kB,WRITE_SIZE,4\n")
+    bench.counters_summary([str(f)])
+    import json
+    out = json.loads(capsys.readouterr().out)
+    assert out["kA"]["dispatches"] == 2 and out["kA"]["FETCH_SIZE"] == pytest.approx(30.0)
+    assert out["kB"]["WRITE_SIZE"] == pytest.approx(4.0)

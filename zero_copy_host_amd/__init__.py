@@ -23,7 +23,8 @@ STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HO
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
            "attn_prefill_variant", "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "kv_paged_alloc_host", "kv_paged_free_host",
            "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
-           "dkv_rmsnorm", "dkv_linear", "dkv_swiglu", "dkv_hostlink_stream", "dkv_last_error", "dkv_version")
+           "dkv_rmsnorm", "dkv_linear", "dkv_swiglu", "dkv_hostlink_stream", "dkv_timing", "dkv_timing_read",
+           "dkv_last_error", "dkv_version")
 PAGE_TOKENS = 16
 PREFILL_VARIANTS = {"fused": 0, "naive": 1, "separate": 2, "staged": 3, "persistent": 4}
 DECODE_VARIANTS = {"zerocopy": 0, "staged": 1}
@@ -86,12 +87,14 @@ def lib() -> ctypes.CDLL:
         L.dkv_linear.argtypes = [VP, VP, VP, VP, I32, I32, I32, I32, VP]
         L.dkv_swiglu.argtypes = [VP, VP, I32, I32, I32, VP]
         L.dkv_hostlink_stream.argtypes = [VP, SZ, I32, I32, VP]
+        L.dkv_timing.argtypes = [I32]
+        L.dkv_timing_read.argtypes = [P(ctypes.c_float), P(I32), I32]
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
         for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
                      "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
                      "attn_prefill_paged", "attn_decode_paged", "dkv_rmsnorm", "dkv_linear", "dkv_swiglu",
-                     "dkv_hostlink_stream"):
+                     "dkv_hostlink_stream", "dkv_timing", "dkv_timing_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -471,6 +474,24 @@ def swiglu(gate_up, y, stream=None) -> None:
 def hostlink_stream(host_ptr: int, nbytes: int, mode: str, n_wg: int = 1024, stream=None) -> None:
     """Kernel streaming read ("read") or write ("write") of pinned host memory."""
     _check(lib().dkv_hostlink_stream(host_ptr, nbytes, {"read": 0, "write": 1}[mode], n_wg, _stream(stream)))
+
+
+TIMED_PHASES = ("projection", "prefill_attention", "decode_qproj", "decode_attention", "decode_combine")
+
+
+def timing(enable: bool) -> None:
+    """Start (True) or stop (False) recording HIP events around the library's kernel phases;
+    either drops what was recorded."""
+    _check(lib().dkv_timing(1 if enable else 0))
+
+
+def timing_read() -> dict:
+    """{phase: (milliseconds, launches)} summed over the calls made while timing was on."""
+    n = len(TIMED_PHASES)
+    ms = (ctypes.c_float * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(lib().dkv_timing_read(ms, cnt, n))
+    return {name: (float(ms[i]), int(cnt[i])) for i, name in enumerate(TIMED_PHASES)}
 
 
 def version() -> int:

@@ -156,6 +156,46 @@ bool xcd_placement() {
   return g_cus == 256 && g_xccs == 8;
 }
 
+// ---- kernel timing on the caller's stream (dkv_timing): HIP events around each phase's launches
+enum TimedPhase { kPhaseProj = 0, kPhaseAttn = 1, kPhaseQproj = 2, kPhaseDecode = 3, kPhaseCombine = 4, kPhases = 5 };
+struct TimedSpan {
+  int phase, launches;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimedSpan> g_spans;
+
+// Records an event on s if timing is on; the events of a span bracket `launches` launches of one
+// phase. Event failures only lose the measurement.
+struct PhaseTimer {
+  hipStream_t s;
+  int phase, launches = 0;
+  hipEvent_t start = nullptr;
+  PhaseTimer(hipStream_t s_, int phase_) : s(s_), phase(phase_) {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    if (!g_timing_on) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventRecord(start, s) != hipSuccess) {
+      (void)hipGetLastError();
+      start = nullptr;
+    }
+  }
+  ~PhaseTimer() {
+    if (start) (void)hipEventDestroy(start);   // a launch failed before done()
+  }
+  void done(int n) {
+    if (!start) return;
+    hipEvent_t stop = nullptr;
+    if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    g_spans.push_back(TimedSpan{phase, n, start, stop});
+    start = nullptr;
+  }
+};
+
 // ---- decode plan: equal key chunks for every workgroup, whatever the lengths
 struct DecodePlan {
   int chunk;
@@ -333,8 +373,10 @@ int run_append(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   a.host_out = 1;
   a.table = pg.table;
   a.max_pages = pg.max_pages;
+  PhaseTimer tp(s, kPhaseProj);
   hipError_t e = f(a, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
+  tp.done(1);
   return DKV_OK;
 }
 
@@ -393,10 +435,20 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   for (int b = 0; b <= batch; ++b) ca.split_begin[b] = p.split_begin[b];
 
   hipError_t e;
-  if (a.qf && (e = fq(a, s)) != hipSuccess) return hip_fail(e, "query projection launch");
+  if (a.qf) {
+    PhaseTimer tq(s, kPhaseQproj);
+    if ((e = fq(a, s)) != hipSuccess) return hip_fail(e, "query projection launch");
+    tq.done(1);
+  }
+  PhaseTimer td(s, kPhaseDecode);
   e = fd(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (!a.direct && (e = fc(ca, s)) != hipSuccess) return hip_fail(e, "combine launch");
+  td.done(1);
+  if (!a.direct) {
+    PhaseTimer tc(s, kPhaseCombine);
+    if ((e = fc(ca, s)) != hipSuccess) return hip_fail(e, "combine launch");
+    tc.done(1);
+  }
   return DKV_OK;
 }
 
@@ -429,8 +481,10 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   pa.host_out = !fused;
   pa.table = pg.table;
   pa.max_pages = pg.max_pages;
+  PhaseTimer tp(s, kPhaseProj);
   hipError_t e = fp(pa, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
+  tp.done(1);
 
   AttnArgs aa;
   memset(&aa, 0, sizeof(aa));
@@ -462,8 +516,11 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which
   // halves the launches every query tile makes and the running-state traffic they cost.
   const int group = aa.xcd_group && P % 8 == 0 ? 8 : P;
+  PhaseTimer ta(s, kPhaseAttn);
+  int n_attn = 0;
   auto launch = [&]() -> int {
     const hipError_t le = fa(aa, s);
+    ++n_attn;
     return le == hipSuccess ? DKV_OK : hip_fail(le, "attention launch");
   };
   for (int pair0 = 0; pair0 < P; pair0 += group) {
@@ -561,6 +618,7 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
       if (st) return st;
     }
   }
+  ta.done(n_attn);
   return DKV_OK;
 }
 
@@ -750,6 +808,37 @@ extern "C" {
 int32_t dkv_version(void) { return 100; }
 
 const char* dkv_last_error(void) { return g_err.c_str(); }
+
+int dkv_timing(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  for (TimedSpan& sp : g_spans) {
+    (void)hipEventDestroy(sp.start);
+    (void)hipEventDestroy(sp.stop);
+  }
+  g_spans.clear();
+  g_timing_on = enable != 0;
+  return DKV_OK;
+}
+
+int dkv_timing_read(float* ms, int32_t* launches, int32_t n) {
+  if (!ms || !launches || n <= 0) return fail(DKV_ERR_INVALID_ARG, "ms and launches must hold n > 0 values");
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.f;
+    launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  for (const TimedSpan& sp : g_spans) {
+    hipError_t e = hipEventSynchronize(sp.stop);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, sp.start, sp.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing event");
+    if (sp.phase < n) {
+      ms[sp.phase] += t;
+      launches[sp.phase] += sp.launches;
+    }
+  }
+  return DKV_OK;
+}
 
 int kv_alloc_host(dkv_cache* out, int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t capacity,
                   int32_t dtype) {
