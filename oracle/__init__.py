@@ -22,14 +22,21 @@ Where the pages leave a step open, the readings taken are:
 - causal alignment: new token t of sequence b sits at absolute position past_len[b] + t
   and sees keys 0 .. past_len[b] + t, itself included (a decode step attends to the key
   it has just appended);
-- no RoPE, no bias, no output projection; W is stored [D, H·d] and applied as X·W;
-  head h occupies columns [h·d, (h+1)·d);
+- no bias and no output projection, and no RoPE in the layer as the pages give it
+  (rope_theta = 0; the rotary embedding below serves the decoder stack around the layer);
+  W is stored [D, H·d] and applied as X·W; head h occupies columns [h·d, (h+1)·d);
 - rounding happens only where the layer stores: appended cache rows are rounded to the
   cache dtype (round to nearest, ties to even) and the attention reads the rounded
   rows; Q and the output are kept in fp64 here.
 
 Arrays: X [B, T, D]; Wq [D, Hq·d]; Wk, Wv [D, Hkv·d]; caches [B, Hkv, cap, d]
 (float32 arrays whose values are exact in the cache dtype, or fp64); past_len int [B].
+
+Rotary position embedding (for the decoder stack around the layer; the pages' layer has none):
+with rope_theta > 0, q and the new k are rotated at their absolute positions before the attention
+and the append. Pairs (i, i + d/2) of each head, i < d/2, turn by the angle p * theta^(-2i/d):
+  y_i = x_i cos - x_{i+d/2} sin,  y_{i+d/2} = x_{i+d/2} cos + x_i sin,
+the rotate-half form of the common Llama-family decoder.
 
 A paged cache (16-token pages and a table from a sequence's logical pages to physical
 pages — "DirectKV Guide: Zero-Copy KV Offloading on GH200 & GB200", section "End-to-End
@@ -119,19 +126,39 @@ def attention(q, kc, vc, past_len, t_index=None, return_lse: bool = False):
     return (out, lse) if return_lse else out
 
 
-def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads: int, dtype: str, t_index=None):
+def rope(x, positions, theta: float) -> np.ndarray:
+    """Rotary position embedding of x [B, n, H, d] at absolute positions [B, n], in fp64:
+    pair (i, i + d/2) of every head turns by positions * theta^(-2i/d)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv_freq = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)          # [d/2]
+    ang = np.asarray(positions, dtype=np.float64)[..., None, None] * inv_freq          # [B, n, 1, d/2]
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads: int, dtype: str, t_index=None,
+               rope_theta: float = 0.0):
     """One layer step: project K/V of the T new tokens, append them to the caches
     (modified in place), then attend for the new tokens t_index (default all).
+    With rope_theta > 0, q and the new k are rotated at positions past_len[b] + t first.
     Returns O [B, n, Hq, d] in fp64."""
     x = np.asarray(x)
     B, T, D = x.shape
     Hkv, d = kc.shape[1], kc.shape[3]
     kn = project(x, wk).reshape(B, T, Hkv, d)
     vn = project(x, wv).reshape(B, T, Hkv, d)
+    pos = np.asarray(past_len, dtype=np.int64)[:, None] + np.arange(T)[None, :]          # [B, T]
+    if rope_theta:
+        kn = rope(kn, pos, rope_theta)
     append(kc, kn, past_len, dtype)
     append(vc, vn, past_len, dtype)
     ts = np.arange(T) if t_index is None else np.asarray(t_index, dtype=np.int64)
     q = project(x[:, ts, :], wq).reshape(B, len(ts), n_q_heads, d)
+    if rope_theta:
+        q = rope(q, pos[:, ts], rope_theta)
     return attention(q, kc, vc, past_len, ts)
 
 
@@ -180,7 +207,8 @@ def swiglu(gu) -> np.ndarray:
     return silu(gu[..., :F]) * gu[..., F:]
 
 
-def decode_stack_step(h, layers, caches, past_len, n_q_heads: int, dtype: str, eps: float) -> np.ndarray:
+def decode_stack_step(h, layers, caches, past_len, n_q_heads: int, dtype: str, eps: float,
+                      rope_theta: float = 0.0) -> np.ndarray:
     """One decode step of a stack of pre-norm decoder layers on hidden states h [B, D]:
     h <- h + attn(rmsnorm(h)) @ Wo;  h <- h + swiglu(rmsnorm(h) @ W_gu) @ W_down.
     layers: dicts of [in, out] weights (wq, wk, wv, wo, w_gu, w_down, g_attn, g_mlp);
@@ -191,7 +219,8 @@ def decode_stack_step(h, layers, caches, past_len, n_q_heads: int, dtype: str, e
     B, D = h.shape
     for lw, (kc, vc) in zip(layers, caches):
         a = round_to_dtype(rmsnorm(h, lw["g_attn"], eps), dtype)
-        o = layer_step(a[:, None, :], lw["wq"], lw["wk"], lw["wv"], kc, vc, past_len, n_q_heads, dtype)
+        o = layer_step(a[:, None, :], lw["wq"], lw["wk"], lw["wv"], kc, vc, past_len, n_q_heads, dtype,
+                       rope_theta=rope_theta)
         o = round_to_dtype(o.reshape(B, -1), dtype)
         h = round_to_dtype(h + project(o, lw["wo"]), dtype)
         m = round_to_dtype(rmsnorm(h, lw["g_mlp"], eps), dtype)

@@ -50,9 +50,24 @@ def _frac(v) -> Fraction:
     return Fraction(float(v))
 
 
-def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads, dtype):
+def rotate(vec, pos, theta):
+    """Rotary embedding of one head vector (floats) at position pos: element i < d/2 and element
+    i + d/2 turn together by pos * theta ** (-2 i / d) (math.cos / math.sin of a Python float)."""
+    d = len(vec)
+    half = d // 2
+    out = list(vec)
+    for i in range(half):
+        a = pos * theta ** (-2.0 * i / d)
+        c, s = math.cos(a), math.sin(a)
+        out[i] = vec[i] * c - vec[i + half] * s
+        out[i + half] = vec[i + half] * c + vec[i] * s
+    return out
+
+
+def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads, dtype, rope_theta=0.0):
     """x nested [B][T][D]; w [D][cols]; kc/vc nested [B][Hkv][cap][d] of floats
-    (modified in place). Returns out as nested [B][T][Hq][d] floats."""
+    (modified in place). Returns out as nested [B][T][Hq][d] floats. With rope_theta, q and
+    the new k are rotated (in floats) at positions past_len[b] + t before the rounding."""
     B, T, D = len(x), len(x[0]) if x else 0, len(x[0][0]) if x and x[0] else 0
     Hkv = len(kc[0])
     d = len(kc[0][0][0])
@@ -65,8 +80,11 @@ def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads, dtype):
     for b in range(B):
         for t in range(T):
             for g in range(Hkv):
+                kvec = [proj(x[b][t], wk, g * d + i) for i in range(d)]
+                if rope_theta:
+                    kvec = [Fraction(v) for v in rotate([float(v) for v in kvec], past_len[b] + t, rope_theta)]
                 for i in range(d):
-                    kval = representable_round(proj(x[b][t], wk, g * d + i), dtype)
+                    kval = representable_round(kvec[i], dtype)
                     vval = representable_round(proj(x[b][t], wv, g * d + i), dtype)
                     kc[b][g][past_len[b] + t][i] = float(kval)
                     vc[b][g][past_len[b] + t][i] = float(vval)
@@ -78,6 +96,8 @@ def layer_step(x, wq, wk, wv, kc, vc, past_len, n_q_heads, dtype):
         for h in range(n_q_heads):
             g = h // G
             q = [[float(proj(x[b][t], wq, h * d + i)) for i in range(d)] for t in range(T)]
+            if rope_theta:
+                q = [rotate(q[t], L + t, rope_theta) for t in range(T)]
             # full score matrix with the causal mask applied as -inf
             S = [[(math.fsum(q[t][i] * kc[b][g][j][i] for i in range(d)) / math.sqrt(d))
                   if j <= L + t else -math.inf for j in range(nk)] for t in range(T)]

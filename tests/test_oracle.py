@@ -468,3 +468,98 @@ def test_decode_stack_with_zero_output_weights_keeps_h():
     assert np.array_equal(got, h.astype(np.float64))
     for b, L in enumerate(past):
         assert not np.array_equal(caches[0][0][b, :, L], before[b, :, L])
+
+
+# ---------------------------------------------------------------- rotary position embedding
+
+def _heads(seed, B=2, n=5, H=3, d=8):
+    return np.random.default_rng(seed).standard_normal((B, n, H, d))
+
+
+def test_rope_at_position_zero_is_the_identity():
+    x = _heads(60)
+    assert np.array_equal(oracle.rope(x, np.zeros((2, 5)), 10000.0), x)
+
+
+def test_rope_turns_pairs_i_and_i_plus_half_only():
+    """A vector with one nonzero component i < d/2 stays in the plane of components i and
+    i + d/2; the first pair (frequency theta^0 = 1) turns by exactly p radians."""
+    d, p = 8, 7.0
+    for i in range(d // 2):
+        x = np.zeros((1, 1, 1, d))
+        x[..., i] = 1.0
+        y = oracle.rope(x, np.array([[p]]), 500000.0)[0, 0, 0]
+        others = [j for j in range(d) if j not in (i, i + d // 2)]
+        assert np.all(y[others] == 0.0)
+        np.testing.assert_allclose(y[i] ** 2 + y[i + d // 2] ** 2, 1.0, rtol=1e-15)
+    x = np.zeros((1, 1, 1, d))
+    x[..., 0] = 1.0
+    y = oracle.rope(x, np.array([[p]]), 500000.0)[0, 0, 0]
+    np.testing.assert_allclose([y[0], y[d // 2]], [math.cos(p), math.sin(p)], rtol=0, atol=1e-15)
+    x = np.zeros((1, 1, 1, d))
+    x[..., d // 2] = 1.0
+    y = oracle.rope(x, np.array([[p]]), 500000.0)[0, 0, 0]
+    np.testing.assert_allclose([y[0], y[d // 2]], [-math.sin(p), math.cos(p)], rtol=0, atol=1e-15)
+
+
+def test_rope_frequencies_fall_geometrically():
+    """At position 1 pair i turns by theta^(-2i/d): successive angles have the constant ratio
+    theta^(-2/d), read back with atan2 from unit vectors (theta = 10000, d = 8: ratio 0.1)."""
+    d = 8
+    angles = []
+    for i in range(d // 2):
+        x = np.zeros((1, 1, 1, d))
+        x[..., i] = 1.0
+        y = oracle.rope(x, np.array([[1.0]]), 10000.0)[0, 0, 0]
+        angles.append(math.atan2(y[i + d // 2], y[i]))
+    np.testing.assert_allclose(angles[0], 1.0, rtol=1e-15)
+    np.testing.assert_allclose(np.array(angles[1:]) / np.array(angles[:-1]), 0.1, rtol=1e-12)
+
+
+def test_rope_composes_and_inverts():
+    x = _heads(61)
+    a = np.arange(10).reshape(2, 5) * 37.0
+    b = np.arange(10).reshape(2, 5) * 11.0 + 3.0
+    th = 500000.0
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, a, th), b, th), oracle.rope(x, a + b, th), atol=1e-12)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, a, th), -a, th), x, atol=1e-12)
+
+
+def test_rope_preserves_norms_and_depends_on_relative_position_only():
+    q, k = _heads(62), _heads(63)
+    th = 10000.0
+    pq = np.array([[3, 50, 700, 9000, 131071]] * 2, dtype=np.float64)
+    pk = pq - np.array([[0, 7, 1, 4096, 65536]] * 2)
+    rq, rk = oracle.rope(q, pq, th), oracle.rope(k, pk, th)
+    np.testing.assert_allclose(np.linalg.norm(rq, axis=-1), np.linalg.norm(q, axis=-1), rtol=1e-13)
+    dot = np.einsum("bnhd,bnhd->bnh", rq, rk)
+    for shift in (1.0, 12345.0):
+        dot2 = np.einsum("bnhd,bnhd->bnh", oracle.rope(q, pq + shift, th), oracle.rope(k, pk + shift, th))
+        np.testing.assert_allclose(dot2, dot, rtol=1e-9, atol=1e-9)
+
+
+def _lists(*arrays):
+    return [np.asarray(a, dtype=np.float64).tolist() for a in arrays]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_layer_with_rope_matches_brute_force(dtype):
+    x, wq, wk, wv, kc, vc, past = _random_layer(64, 2, 3, [4, 9], 16, 4, 2, 8, dtype)
+    bk, bv = _lists(kc, vc)
+    got = oracle.layer_step(x, wq, wk, wv, kc, vc, past, 4, dtype, rope_theta=10000.0)
+    ref = brute.layer_step(*_lists(x, wq, wk, wv), bk, bv, [int(p) for p in past], 4, dtype, rope_theta=10000.0)
+    np.testing.assert_allclose(got, np.array(ref), rtol=1e-11, atol=1e-12)
+    assert np.array_equal(kc.astype(np.float64), np.array(bk))   # the same rotated, rounded rows
+
+
+def test_rope_layer_phase_consistency():
+    """With RoPE the positions come from past_len: two prefill chunks give the single prefill's
+    outputs and cache rows (fp64, within rounding order)."""
+    x, wq, wk, wv, kc, vc, past = _random_layer(65, 1, 6, [5], 16, 4, 2, 8, "f32")
+    kc1, vc1 = kc.copy(), vc.copy()
+    o1 = oracle.layer_step(x, wq, wk, wv, kc1, vc1, past, 4, "f32", rope_theta=10000.0)
+    kc2, vc2 = kc.copy(), vc.copy()
+    a = oracle.layer_step(x[:, :2], wq, wk, wv, kc2, vc2, past, 4, "f32", rope_theta=10000.0)
+    b = oracle.layer_step(x[:, 2:], wq, wk, wv, kc2, vc2, past + 2, 4, "f32", rope_theta=10000.0)
+    np.testing.assert_allclose(np.concatenate([a, b], axis=1), o1, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(kc1, kc2)

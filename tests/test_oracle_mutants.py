@@ -31,6 +31,13 @@ MUTANTS = [
     ("stack_no_residual", 'h = round_to_dtype(h + project(o, lw["wo"]), dtype)', 'h = round_to_dtype(project(o, lw["wo"]), dtype)'),
     ("stack_activation_unrounded", "act = round_to_dtype(swiglu(gu), dtype)", "act = swiglu(gu)"),
     ("stack_wrong_norm_weight", 'rmsnorm(h, lw["g_mlp"], eps)', 'rmsnorm(h, lw["g_attn"], eps)'),
+    ("rope_sin_sign", "[lo * c - hi * s, hi * c + lo * s]", "[lo * c + hi * s, hi * c - lo * s]"),
+    ("rope_interleaved_pairs", "lo, hi = x[..., :half], x[..., half:]", "lo, hi = x[..., 0::2], x[..., 1::2]"),
+    ("rope_frequency_exponent", "(-2.0 * np.arange(half, dtype=np.float64) / d)",
+     "(-1.0 * np.arange(half, dtype=np.float64) / d)"),
+    ("rope_position_off_by_one", "pos = np.asarray(past_len, dtype=np.int64)[:, None] + np.arange(T)[None, :]",
+     "pos = np.asarray(past_len, dtype=np.int64)[:, None] + 1 + np.arange(T)[None, :]"),
+    ("rope_query_unrotated", "q = rope(q, pos[:, ts], rope_theta)", "q = q"),
 ]
 
 
