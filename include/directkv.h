@@ -185,6 +185,26 @@ int attn_decode(const dkv_cache* c, const void* x, const void* wq, const void* w
                 int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * attn_prefill and attn_decode with a rotary position embedding, for the multi-layer decode loop
+ * around the layer (the pages' layer itself has no positional encoding): q and the new k are
+ * rotated at their absolute positions p = past_len[b] + t before attention and before k is rounded
+ * and appended. Pair (i, i + d/2) of each head, i < d/2, turns by p * rope_theta^(-2i/d):
+ * y_i = x_i cos - x_{i+d/2} sin, y_{i+d/2} = x_{i+d/2} cos + x_i sin (the rotate-half form of
+ * the Llama-family decoder; Llama 3 uses rope_theta = 500000). Angles are formed in fp64. Cached
+ * keys are the rotated ones, so calls on one cache must all use RoPE with the same base. Arguments,
+ * workspace (attn_workspace_bytes phase 0 / 1) and errors as attn_prefill / attn_decode, plus
+ * INVALID_ARG unless 1 < rope_theta <= 1e30.
+ */
+int attn_prefill_rope(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                      const void* wv, const int32_t* past_len, int32_t batch, int32_t T,
+                      int32_t D, int32_t n_q_heads, void* out, void* ws, size_t ws_bytes,
+                      double rope_theta, void* stream);
+int attn_decode_rope(const dkv_cache* c, const void* x, const void* wq, const void* wk,
+                     const void* wv, const int32_t* past_len, int32_t batch, int32_t D,
+                     int32_t n_q_heads, void* out, void* ws, size_t ws_bytes, double rope_theta,
+                     void* stream);
+
+/*
  * attn_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): the same kernels and result as attn_decode
  * (bitwise), with no workspace argument. Its scratch (split partials and projected queries,

@@ -59,7 +59,7 @@ class GpuLayer:
         self.wk = to_dev(c["wk"].T, dt)
         self.wv = to_dev(c["wv"].T, dt)
 
-    def prefill(self, x, past_len, variant=None):
+    def prefill(self, x, past_len, variant=None, rope_theta=0.0):
         import torch
         c = self.c
         B, T, D = x.shape
@@ -68,14 +68,15 @@ class GpuLayer:
         nb = self.dkv.workspace_bytes("prefill", self.cache, B, T, c["Hq"])
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
         if variant is None:
-            self.dkv.attn_prefill(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws)
+            self.dkv.attn_prefill(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws,
+                                  rope_theta=rope_theta)
         else:
             self.dkv.attn_prefill_variant(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws,
                                           variant)
         torch.cuda.synchronize()
         return from_dev(out).reshape(B, T, c["Hq"], c["d"])
 
-    def decode(self, x, past_len):
+    def decode(self, x, past_len, rope_theta=0.0):
         import torch
         c = self.c
         B, _, D = x.shape
@@ -83,7 +84,8 @@ class GpuLayer:
         out = torch.empty((B, 1, c["Hq"] * c["d"]), dtype=torch_dtype(c["dtype"]), device="cuda")
         nb = self.dkv.workspace_bytes("decode", self.cache, B, 1, c["Hq"])
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        self.dkv.attn_decode(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws)
+        self.dkv.attn_decode(self.cache, xd, self.wq, self.wk, self.wv, past_len, c["Hq"], out, ws,
+                             rope_theta=rope_theta)
         torch.cuda.synchronize()
         return from_dev(out).reshape(B, 1, c["Hq"], c["d"])
 
@@ -103,10 +105,10 @@ class GpuLayer:
         self.cache.free()
 
 
-def oracle_step(case, x, past_len, kc, vc, t_index=None):
+def oracle_step(case, x, past_len, kc, vc, t_index=None, rope_theta=0.0):
     """Oracle layer step on float32 cache copies (modified in place)."""
     return oracle.layer_step(x, case["wq"], case["wk"], case["wv"], kc, vc, past_len, case["Hq"],
-                             case["dtype"], t_index=t_index)
+                             case["dtype"], t_index=t_index, rope_theta=rope_theta)
 
 
 def compare(got, ref, dtype, what=""):

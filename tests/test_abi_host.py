@@ -147,9 +147,11 @@ def test_workspace_sizes(dkv):
     ws = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
     e = 2
     # queries + new K + new V + two fp32 running states (past keys, this step's own keys): per 32
-    # query rows, 64 lanes x (d/32 * 16 accumulators + m + l)
+    # query rows, 64 lanes x (d/32 * 16 accumulators + m + l); then the rotary (cos, sin) fp32 table
+    # of every new row's d/2 pairs
     want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 2 * 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
-    assert want <= ws <= want + 5 * 256
+    want += 8192 * 64 * 2 * 4
+    assert want <= ws <= want + 6 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
     # decode: fp32 partials (o, m, l) for at most 2 * (2 * 256 / Hkv) + B + 1 splits (the split
     # target doubles for short chunks), then the fp32 queries [B][Hq*d] the pre-pass projects
@@ -333,3 +335,25 @@ def test_binding_refuses_bad_decode_loop_tensors(dkv):
         dkv.swiglu(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, 32, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="unsupported dtype"):
         dkv.swiglu(torch.zeros(4, 64, dtype=torch.int32), torch.zeros(4, 32, dtype=torch.int32))
+
+
+def test_rope_base_validation(dkv):
+    """attn_prefill_rope / attn_decode_rope take a finite rotary base above 1; anything else is
+    INVALID_ARG before any workspace, memory or HIP check."""
+    L = dkv.lib()
+    c = _fake_cache(dkv, B=2, Hkv=2, d=128, cap=4096)
+    x = w = out = ws = 0x10000
+    lens, lp = _lens([10, 20])
+    for theta in (0.0, 1.0, 0.5, -10000.0, float("nan"), float("inf"), 1e31):
+        assert L.attn_prefill_rope(ctypes.byref(c), x, w, w, w, lp, 2, 16, 256, 8, out, ws, 1 << 30, theta,
+                                   None) == -1, theta
+        assert "rope_theta" in _err(dkv)
+        assert L.attn_decode_rope(ctypes.byref(c), x, w, w, w, lp, 2, 256, 8, out, ws, 1 << 30, theta, None) == -1
+        assert "rope_theta" in _err(dkv)
+    # a good base goes on to the next check (here: the workspace is too small)
+    assert L.attn_prefill_rope(ctypes.byref(c), x, w, w, w, lp, 2, 16, 256, 8, out, ws, 16, 500000.0, None) == -6
+    assert L.attn_decode_rope(ctypes.byref(c), x, w, w, w, lp, 2, 256, 8, out, ws, 16, 10000.0, None) == -6
+    # the usual argument checks come first
+    assert L.attn_prefill_rope(ctypes.byref(c), x, w, w, w, lp, 2, 16, 256, 7, out, ws, 1 << 30, 500000.0,
+                               None) == -1
+    assert "rope_theta" not in _err(dkv)

@@ -1,12 +1,16 @@
 """The decode-loop kernels (RMSNorm, linear with residual, SwiGLU) and a two-layer decoder stack
-(DecodeStack: one host KV cache per layer) against the oracle, through the C ABI.
+(DecodeStack: one host KV cache per layer, with and without the rotary embedding) against the
+oracle, through the C ABI.
 
 Tolerances. Each kernel accumulates in fp32 and rounds once to the storage dtype, as the oracle
 (fp64) does at the same points: a single kernel is within 1 ulp of the dtype plus the fp32
-accumulation error (K·2⁻²⁴·Σ|x||w| for a K-term product). A stack of layers compounds the
-per-layer attention tolerance (max-abs 2e-2 / mean-abs 2e-3 for bf16, 1e-5 for fp32) through
-the residual stream, so two layers are held to three times it, relative to max(1, rms) of the
-reference hidden state.
+accumulation error (K·2⁻²⁴·Σ|x||w| for a K-term product). A decoder layer is checked on its own,
+fed the GPU's own input to that layer, so errors do not compound across layers: its output
+differs from the oracle's by the attention output's error carried through Wo (Wo ~ N(0, 1/(Hq·d))
+keeps a random error's size: the layer's attention tolerance, max-abs 2e-2 / mean-abs 2e-3 for
+bf16, 1e-5 for fp32) plus the two residual sums' roundings, each of which can land one ulp of
+the hidden state away from the oracle's; the MLP's roundings feed the second sum the same way.
+The whole stack is then the chain of its layers, bit for bit.
 """
 import numpy as np
 import pytest
@@ -90,52 +94,90 @@ def test_helpers_reject_bad_arguments():
     assert L.dkv_rmsnorm(None, b.data_ptr(), a.data_ptr(), 4, 64, ctypes.c_float(1e-5), 2, None) == -1
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_two_layer_decode_stack(dtype):
-    import torch
-    import zero_copy_host_amd as dkv
-    from zero_copy_host_amd.decode_stack import DecodeStack
-    n_layers, B, D, Hq, Hkv, d, F = 2, 3, 256, 8, 2, 64, 384
-    past = np.array([37, 100, 5], dtype=np.int32)
+def _stack_case(dtype, n_layers=2, B=3, D=256, Hq=8, Hkv=2, d=64, F=384):
+    past = np.array([37, 100, 5], dtype=np.int32)[:B]
     cap = 192
     dr = synth.Draw(504)
     layers = synth.stack_weights(dr, n_layers, D, Hq, Hkv, d, F, dtype)
-    caches_o, caches = [], []
+    caches_o = []
     for _ in range(n_layers):
         kc = np.zeros((B, Hkv, cap, d), dtype=np.float32)
         vc = np.zeros((B, Hkv, cap, d), dtype=np.float32)
         synth.fill_past(dr, kc, vc, past, dtype)
         caches_o.append((kc, vc))
-        c = dkv.HostKVCache(B, Hkv, d, cap, dtype)
+    h = dr.normal((B, D), 1.0, dtype)
+    return dict(layers=layers, caches_o=caches_o, h=h, past=past, B=B, D=D, Hq=Hq, Hkv=Hkv, d=d, cap=cap)
+
+
+def _host_caches(case, dtype):
+    import zero_copy_host_amd as dkv
+    out = []
+    for kc, vc in case["caches_o"]:
+        c = dkv.HostKVCache(case["B"], case["Hkv"], case["d"], case["cap"], dtype)
         c.k[...] = synth.to_storage(kc, dtype)
         c.v[...] = synth.to_storage(vc, dtype)
-        caches.append(c)
-    h = dr.normal((B, D), 1.0, dtype)
-    dev_layers = [{"wq": _dev(lw["wq"].T, dtype), "wk": _dev(lw["wk"].T, dtype), "wv": _dev(lw["wv"].T, dtype),
-                   "wo": _dev(lw["wo"].T, dtype), "w_gu": _dev(lw["w_gu"].T, dtype),
-                   "w_down": _dev(lw["w_down"].T, dtype), "g_attn": _dev(lw["g_attn"], dtype),
-                   "g_mlp": _dev(lw["g_mlp"], dtype)} for lw in layers]
-    try:
-        stack = DecodeStack(dev_layers, caches, Hq, eps=1e-5)
-        hd = _dev(h, dtype)
-        stack.step(hd, past)
-        torch.cuda.synchronize()
-        got = from_dev(hd)
-        new_rows = [(synth.from_storage(c.k, dtype), synth.from_storage(c.v, dtype)) for c in caches]
-    finally:
-        for c in caches:
-            c.free()
-    ref = oracle.decode_stack_step(h, layers, caches_o, past, Hq, dtype, 1e-5)
-    scale = max(1.0, float(np.sqrt(np.mean(ref ** 2))))
-    err = np.abs(got - ref)
-    tmax, tmean = {"bf16": (6e-2, 6e-3), "f32": (3e-5, 3e-5)}[dtype]
-    print(f"stack {dtype}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} rms(ref)={scale:.3f}", flush=True)
-    assert err.max() <= tmax * scale and err.mean() <= tmean * scale
-    # every layer appended the new token's K/V at row past_len[b] and touched nothing else
-    for (kg, vg), (ko, vo) in zip(new_rows, caches_o):
+        out.append(c)
+    return out
+
+
+def _dev_layer(lw, dtype):
+    return {"wq": _dev(lw["wq"].T, dtype), "wk": _dev(lw["wk"].T, dtype), "wv": _dev(lw["wv"].T, dtype),
+            "wo": _dev(lw["wo"].T, dtype), "w_gu": _dev(lw["w_gu"].T, dtype),
+            "w_down": _dev(lw["w_down"].T, dtype), "g_attn": _dev(lw["g_attn"], dtype),
+            "g_mlp": _dev(lw["g_mlp"], dtype)}
+
+
+@pytest.mark.parametrize("rope_theta", [0.0, 500000.0], ids=["norope", "rope"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_two_layer_decode_stack(dtype, rope_theta):
+    import torch
+    from zero_copy_host_amd.decode_stack import DecodeStack
+    case = _stack_case(dtype)
+    layers, past, Hq = case["layers"], case["past"], case["Hq"]
+    dev_layers = [_dev_layer(lw, dtype) for lw in layers]
+    tmax, tmean = {"bf16": (2e-2, 2e-3), "f32": (1e-5, 1e-5)}[dtype]
+
+    # each layer alone (a one-layer stack on fresh caches), fed the GPU's output of the layer before
+    h_in = case["h"]
+    chain = []
+    for i, lw in enumerate(layers):
+        caches = _host_caches(case, dtype)
+        try:
+            one = DecodeStack([dev_layers[i]], [caches[i]], Hq, eps=1e-5, rope_theta=rope_theta)
+            hd = _dev(h_in, dtype)
+            one.step(hd, past)
+            torch.cuda.synchronize()
+            h_out = from_dev(hd)
+            kg, vg = synth.from_storage(caches[i].k, dtype), synth.from_storage(caches[i].v, dtype)
+        finally:
+            for c in caches:
+                c.free()
+        ko, vo = case["caches_o"][i][0].copy(), case["caches_o"][i][1].copy()
+        ref = oracle.decode_stack_step(h_in, [lw], [(ko, vo)], past, Hq, dtype, 1e-5, rope_theta=rope_theta)
+        err = np.abs(h_out - ref)
+        ulp = _ulp(ref, dtype)
+        print(f"layer {i} {dtype} rope={rope_theta}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+        assert (err <= tmax + 2 * ulp).all(), f"layer {i}: max-abs {err.max():.3e}"
+        assert err.mean() <= tmean + float(ulp.mean()), f"layer {i}: mean-abs {err.mean():.3e}"
+        # the layer appended the new token's K/V at row past_len[b] and touched nothing else; the
+        # appended rows come from the normed input, computed in fp32 on both sides of one rounding
         for b, L in enumerate(past):
             assert np.array_equal(kg[b, :, :L], ko[b, :, :L]) and np.array_equal(vg[b, :, :L], vo[b, :, :L])
             assert np.all(kg[b, :, L + 1:] == 0) and np.all(vg[b, :, L + 1:] == 0)
-            # the appended rows come from each layer's input, so they carry the stack's error
-            assert np.abs(kg[b, :, L] - ko[b, :, L]).max() <= tmax * scale
-            assert np.abs(vg[b, :, L] - vo[b, :, L]).max() <= tmax * scale
+            assert np.abs(kg[b, :, L] - ko[b, :, L]).max() <= tmax
+            assert np.abs(vg[b, :, L] - vo[b, :, L]).max() <= tmax
+        chain.append(h_out)
+        h_in = h_out
+
+    # the two-layer stack is the chain of its layers, bit for bit
+    caches = _host_caches(case, dtype)
+    try:
+        stack = DecodeStack(dev_layers, caches, Hq, eps=1e-5, rope_theta=rope_theta)
+        hd = _dev(case["h"], dtype)
+        stack.step(hd, past)
+        torch.cuda.synchronize()
+        got = from_dev(hd)
+    finally:
+        for c in caches:
+            c.free()
+    assert np.array_equal(got, chain[-1])

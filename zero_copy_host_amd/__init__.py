@@ -21,7 +21,8 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "CAPACITY", -3: "UNSUPPORTED", -4: "HOST_ALLOC",
           -5: "HIP", -6: "WORKSPACE"}
 EXPORTS = ("kv_alloc_host", "kv_free_host", "kv_append", "attn_workspace_bytes", "attn_prefill",
-           "attn_prefill_variant", "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "kv_paged_alloc_host", "kv_paged_free_host",
+           "attn_prefill_variant", "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "attn_prefill_rope",
+           "attn_decode_rope", "kv_paged_alloc_host", "kv_paged_free_host",
            "attn_paged_workspace_bytes", "kv_paged_append", "attn_prefill_paged", "attn_decode_paged",
            "dkv_rmsnorm", "dkv_linear", "dkv_swiglu", "dkv_hostlink_stream", "dkv_timing", "dkv_timing_read",
            "dkv_last_error", "dkv_version")
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP]
         L.attn_decode_variant.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, VP, I32]
         L.attn_decode_noalloc.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP]
+        D64 = ctypes.c_double
+        L.attn_prefill_rope.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, I32, VP, VP, SZ, D64, VP]
+        L.attn_decode_rope.argtypes = [P(dkv_cache), VP, VP, VP, VP, P(I32), I32, I32, I32, VP, VP, SZ, D64, VP]
         L.kv_paged_alloc_host.argtypes = [P(dkv_paged_cache), I32, I32, I32, I32]
         L.kv_paged_free_host.argtypes = [P(dkv_paged_cache)]
         L.attn_paged_workspace_bytes.argtypes = [I32, P(dkv_paged_cache), I32, I32, I32, I32]
@@ -92,7 +96,8 @@ def lib() -> ctypes.CDLL:
         L.dkv_last_error.restype = ctypes.c_char_p
         L.dkv_version.restype = I32
         for name in ("kv_alloc_host", "kv_free_host", "kv_append", "attn_prefill", "attn_prefill_variant",
-                     "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
+                     "attn_decode", "attn_decode_variant", "attn_decode_noalloc", "attn_prefill_rope", "attn_decode_rope",
+                     "kv_paged_alloc_host", "kv_paged_free_host", "kv_paged_append",
                      "attn_prefill_paged", "attn_decode_paged", "dkv_rmsnorm", "dkv_linear", "dkv_swiglu",
                      "dkv_hostlink_stream", "dkv_timing", "dkv_timing_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -249,13 +254,19 @@ def workspace_bytes(phase: str, cache: HostKVCache, batch: int, T: int, n_q_head
     return int(lib().attn_workspace_bytes(ph, ctypes.byref(cache.desc), batch, T, n_q_heads, None))
 
 
-def attn_prefill(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:
-    """One prefill step of T tokens per sequence; out: [B, T, Hq*d] device tensor."""
+def attn_prefill(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None,
+                 rope_theta: float = 0.0) -> None:
+    """One prefill step of T tokens per sequence; out: [B, T, Hq*d] device tensor. rope_theta > 0
+    rotates q and the new k at positions past_len[b] + t (attn_prefill_rope)."""
     B, T, D = x.shape
     desc = _cache_desc(cache, dkv_cache)
     _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, T, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     nbytes = ws.numel() * ws.element_size()
+    if rope_theta:
+        _check(lib().attn_prefill_rope(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T, D,
+                                       n_q_heads, _ptr(out), _ptr(ws), nbytes, float(rope_theta), _stream(stream)))
+        return
     _check(lib().attn_prefill(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, T, D,
                               n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
@@ -273,13 +284,19 @@ def attn_prefill_variant(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads:
                                       PREFILL_VARIANTS[variant]))
 
 
-def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None) -> None:
-    """One decode step; x: [B, 1, D] (or [B, D]); out: [B, 1, Hq*d] device tensor."""
+def attn_decode(cache: HostKVCache, x, wq, wk, wv, past_len, n_q_heads: int, out, ws, stream=None,
+                rope_theta: float = 0.0) -> None:
+    """One decode step; x: [B, 1, D] (or [B, D]); out: [B, 1, Hq*d] device tensor. rope_theta > 0
+    rotates q and the new k at position past_len[b] (attn_decode_rope)."""
     B, D = x.shape[0], x.shape[-1]
     desc = _cache_desc(cache, dkv_cache)
     _layer_tensors(cache, x, wq, wk, wv, out, ws, n_q_heads, 1, B, D, cache.shape[1], cache.shape[3])
     lens, lp = _lens(past_len, B)
     nbytes = ws.numel() * ws.element_size()
+    if rope_theta:
+        _check(lib().attn_decode_rope(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
+                                      n_q_heads, _ptr(out), _ptr(ws), nbytes, float(rope_theta), _stream(stream)))
+        return
     _check(lib().attn_decode(ctypes.byref(desc), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), lp, B, D,
                              n_q_heads, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 

@@ -267,7 +267,7 @@ bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, i
 
 // ---- prefill workspace layout
 struct PrefillWs {
-  size_t q, k_new, v_new, state, nstate, total;
+  size_t q, k_new, v_new, state, nstate, rope, total;
 };
 
 PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
@@ -280,7 +280,8 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   w.state = w.v_new + round_up((size_t)batch * c->n_kv_heads * T * d * e, 256);
   const size_t sb = round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
   w.nstate = w.state + sb;
-  w.total = w.nstate + sb;
+  w.rope = w.nstate + sb;   // rotary (cos, sin) table of the call's rows (attn_prefill_rope)
+  w.total = w.rope + round_up((size_t)batch * T * (d / 2) * 2 * sizeof(float), 256);
   return w;
 }
 
@@ -382,7 +383,7 @@ int run_append(const dkv_cache* c, const Paging& pg, const void* x, const void* 
 
 int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* wq, const void* wk,
                const void* wv, const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out,
-               void* ws, size_t ws_bytes, hipStream_t s) {
+               void* ws, size_t ws_bytes, hipStream_t s, double rope = 0.0) {
   const bool paged = pg.table != nullptr;
   const size_t need = decode_ws_bytes(c, batch, n_q_heads, paged);
   if (!ws || ws_bytes < need || !aligned16(ws))
@@ -424,6 +425,7 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
   a.max_pages = pg.max_pages;
   for (int b = 0; b < batch; ++b) a.past_len[b] = past_len[b];
   for (int b = 0; b <= batch; ++b) a.split_begin[b] = p.split_begin[b];
+  a.rope_theta = rope;
 
   CombineArgs ca;
   memset(&ca, 0, sizeof(ca));
@@ -454,7 +456,7 @@ int run_decode(const dkv_cache* c, const Paging& pg, const void* x, const void* 
 
 int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void* wq, const void* wk,
                 const void* wv, const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
-                void* out, void* ws, size_t ws_bytes, hipStream_t s, int32_t variant) {
+                void* out, void* ws, size_t ws_bytes, hipStream_t s, int32_t variant, double rope = 0.0) {
   const bool paged = pg.table != nullptr;
   const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads);
   if (!ws || ws_bytes < lay.total || !aligned16(ws))
@@ -481,6 +483,12 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   pa.host_out = !fused;
   pa.table = pg.table;
   pa.max_pages = pg.max_pages;
+  if (rope > 0.0) {
+    float2* cs = reinterpret_cast<float2*>(w + lay.rope);
+    hipError_t re = launch_rope_table(past_len, batch, T, c->head_dim, rope, cs, s);
+    if (re != hipSuccess) return hip_fail(re, "rotary table launch");
+    pa.rope_cs = cs;
+  }
   PhaseTimer tp(s, kPhaseProj);
   hipError_t e = fp(pa, s);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
@@ -936,6 +944,46 @@ int attn_decode_variant(const dkv_cache* c, const void* x, const void* wq, const
                        reinterpret_cast<char*>(ws) + sb, ws_bytes - sb, s)))
     return st;
   return stage_out(c, dev, past_len, 1, s);
+}
+
+namespace {
+int check_rope(double theta) {
+  if (!(theta > 1.0) || theta > 1e30)
+    return fail(DKV_ERR_INVALID_ARG, "rope_theta must be a finite base > 1 (got %g)", theta);
+  return DKV_OK;
+}
+}  // namespace
+
+int attn_prefill_rope(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                      const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads, void* out,
+                      void* ws, size_t ws_bytes, double rope_theta, void* stream) {
+  int st = check_call(c, batch, T, D, past_len, {x, wq, wk, wv, out});
+  if (st) return st;
+  if ((st = check_heads(c, n_q_heads))) return st;
+  if ((st = check_rope(rope_theta))) return st;
+  if (T == 0) return DKV_OK;
+  const size_t need = prefill_layout(c, batch, T, n_q_heads).total;
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  if ((st = check_cache_memory(c))) return st;
+  return run_prefill(c, Paging{}, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, out, ws, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream), DKV_PREFILL_FUSED, rope_theta);
+}
+
+int attn_decode_rope(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,
+                     const int32_t* past_len, int32_t batch, int32_t D, int32_t n_q_heads, void* out, void* ws,
+                     size_t ws_bytes, double rope_theta, void* stream) {
+  int st = check_call(c, batch, 1, D, past_len, {x, wq, wk, wv, out});
+  if (st) return st;
+  if ((st = check_heads(c, n_q_heads))) return st;
+  if (D > kMaxD) return fail(DKV_ERR_UNSUPPORTED, "decode supports D <= %d", kMaxD);
+  if ((st = check_rope(rope_theta))) return st;
+  const size_t need = decode_ws_bytes(c, batch, n_q_heads, false);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, need);
+  if ((st = check_cache_memory(c))) return st;
+  return run_decode(c, Paging{}, x, wq, wk, wv, past_len, batch, D, n_q_heads, out, ws, ws_bytes,
+                    reinterpret_cast<hipStream_t>(stream), rope_theta);
 }
 
 int attn_decode_noalloc(const dkv_cache* c, const void* x, const void* wq, const void* wk, const void* wv,

@@ -179,6 +179,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     project_rows<T, 8>(s_buf, reinterpret_cast<const T*>(a.wv), a.D, g * DH, DH, s_kv + DH, 1.f);
   }
   __syncthreads();
+  if (a.rope_theta > 0.0) {
+    // rotary embedding at this token's position L: the G query heads and (if projected here) the
+    // new key, pair (i, i + d/2) of each head, before the key is rounded and stored
+    constexpr int HALF = DH / 2;
+    const int nvec = G + (has_new ? 1 : 0);
+    for (int idx = tid; idx < nvec * HALF; idx += blockDim.x) {
+      const int h = idx / HALF, i = idx - h * HALF;
+      float* v = h < G ? s_q + h * DH : s_kv;
+      double c, sn;
+      rope_angle_cs(L, i, DH, a.rope_theta, c, sn);
+      const float lo = v[i], hi = v[i + HALF];
+      v[i] = lo * (float)c - hi * (float)sn;
+      v[i + HALF] = hi * (float)c + lo * (float)sn;
+    }
+    __syncthreads();
+  }
   if (has_new) {
     // storer: round to the cache dtype and write host row L; attention below uses the
     // rounded values from LDS, never reading the row back over the link

@@ -128,6 +128,14 @@ __device__ inline size_t host_row(const int32_t* table, int max_pages, int b, in
 
 __device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
+// Rotary angle of pair i (of d/2) at position pos: pos * theta^(-2i/d), in fp64, and its cosine and
+// sine (fp64 library routines with their own argument reduction; a long position turns the first
+// pairs through ~1e5 radians, which fp32 would carry with ~1e-2 radians of error).
+__device__ inline void rope_angle_cs(int pos, int i, int d, double theta, double& c, double& s) {
+  const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)d);
+  sincos(ang, &s, &c);
+}
+
 // Lanes l and l + 32 hold the same query row in the transposed score layout: combine their
 // values with one lane-swap instruction (v_permlane32_swap: result[0] is x with its upper half
 // replaced by the lower half, result[1] x with its lower half replaced by the upper half).
@@ -156,6 +164,8 @@ struct ProjArgs {
   int32_t host_out;         // 1: write the new K/V rows to the host cache (segments 1, 2)
   const int32_t* table;     // paged cache: device block table [B][max_pages]; null = contiguous
   int32_t max_pages;
+  const float2* rope_cs;    // rotary embedding: (cos, sin) of row m = b*T + t, pair i at [m * d/2 + i]
+                            // (rope_table_kernel); null = no rotation. Rotates Q and K (segments 0, 1)
   int32_t past_len[kMaxBatch];
 };
 
@@ -178,6 +188,7 @@ struct DecodeArgs {
   int32_t past_len[kMaxBatch];
   int32_t split_begin[kMaxBatch + 1];  // first global split of sequence b
   int32_t chunk;                       // keys per split
+  double rope_theta;                   // rotary embedding base for q and the new k; 0 = none
 };
 
 struct CombineArgs {
@@ -237,6 +248,11 @@ int attn_rows_per_tile();            // query rows (token x head) per prefill WG
 size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G);
 
 hipError_t launch_hostlink(void* p, size_t bytes, int mode, int n_wg, hipStream_t s);
+
+// (cos, sin) of the rotary angle (past_len[b] + t) * theta^(-2i/d) for every row m = b*T + t of a
+// call and pair i < d/2, into cs[m * d/2 + i] (proj.hip)
+hipError_t launch_rope_table(const int32_t* past_len, int B, int T, int d, double theta, float2* cs,
+                             hipStream_t s);
 
 // decode-loop kernels around the layer (model.hip); dtype as dkv_dtype
 hipError_t launch_rmsnorm(int dtype, const void* x, const void* w, void* y, int rows, int D, float eps,

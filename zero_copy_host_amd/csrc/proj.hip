@@ -19,6 +19,8 @@
 // keeps 2x2 waves of 64x64 tiles with steps of 64. The reduction depth needs D % 64 == 0, which the ABI
 // checks. The epilogue is staged through LDS so every output row leaves as full 16-byte-per-
 // lane contiguous writes (whole host cache lines for K and V).
+#include <algorithm>
+
 #include "dkv_internal.h"
 
 namespace dkv {
@@ -180,25 +182,9 @@ void proj_kernel(const ProjArgs a) {
   }
   if (kt < nk) step(kt, 0, 0);
 
-  // ---- epilogue: round to T into an LDS tile, then write whole rows
-  T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 32 * MB + i * 32 + acc_row(v, lane);
-        const int cc = wn * 32 * NB + j * 32 + (lane & 31);
-        sO[r * C::LDO + cc] = Elem<T>::from_float(acc[i][j][v]);
-      }
-  __syncthreads();
+  // ---- epilogue: round to T into an LDS tile, then write whole rows (16 bytes a lane)
   constexpr int CH = BN / VEC;                   // 16-byte chunks per output row
-  for (int c = tid; c < BM * CH; c += THREADS) {
-    const int r = c / CH, cc = (c % CH) * VEC;
-    const int m = m0 + r, n = n0 + cc;
-    if (m >= a.M || n >= nseg) continue;
-    const uint4 val = *reinterpret_cast<const uint4*>(sO + r * C::LDO + cc);
+  auto store_chunk = [&](const int m, const int n, const uint4 val) __attribute__((always_inline)) {
     if (seg == 0) {
       *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.q_out) + (size_t)m * nseg + n) = val;
     } else {
@@ -213,6 +199,75 @@ void proj_kernel(const ProjArgs a) {
       void* dev = seg == 1 ? a.k_dev : a.v_dev;
       if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
     }
+  };
+
+  if (a.rope_cs != nullptr && seg < 2) {
+    // Rotary embedding of Q and K at positions past_len[b] + t, on the fp32 accumulators before the
+    // rounding: the tile is staged in fp32, a band of wave rows at a time, and each 16-byte output
+    // chunk is formed from its own columns and their partners d/2 away in the same head (a
+    // workgroup's columns start at a multiple of 128 and hold whole heads).
+    constexpr int LDF = BN + 4;                  // padded fp32 staging row
+    constexpr int WROWS = 32 * MB;               // rows of one wave row
+    constexpr int BAND = (C::SMEM / (LDF * 4)) / WROWS >= C::WM ? C::WM : 2;   // wave rows per band
+    static_assert(C::WM % BAND == 0 && BAND * WROWS * LDF * 4 <= C::SMEM, "fp32 staging band");
+    float* sF = reinterpret_cast<float*>(smem);
+    const int half = a.d / 2;
+    for (int band = 0; band < C::WM / BAND; ++band) {
+      if (wm / BAND == band) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = (wm % BAND) * WROWS + i * 32 + acc_row(v, lane);
+              sF[r * LDF + wn * 32 * NB + j * 32 + (lane & 31)] = acc[i][j][v];
+            }
+      }
+      __syncthreads();
+      for (int c = tid; c < BAND * WROWS * CH; c += THREADS) {
+        const int rl = c / CH, cc = (c % CH) * VEC;
+        const int m = m0 + band * BAND * WROWS + rl, n = n0 + cc;
+        if (m >= a.M || n >= nseg) continue;
+        const int hc = n % a.d;
+        const bool low = hc < half;
+        const int ip = low ? hc : hc - half;
+        const float* own = sF + rl * LDF + cc;
+        const float* oth = sF + rl * LDF + (low ? cc + half : cc - half);
+        const float2* cs = a.rope_cs + (size_t)m * half + ip;
+        T res[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float2 w = cs[e];
+          const float y = low ? own[e] * w.x - oth[e] * w.y : own[e] * w.x + oth[e] * w.y;
+          res[e] = Elem<T>::from_float(y);
+        }
+        uint4 val;
+        __builtin_memcpy(&val, res, 16);
+        store_chunk(m, n, val);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 32 * MB + i * 32 + acc_row(v, lane);
+        const int cc = wn * 32 * NB + j * 32 + (lane & 31);
+        sO[r * C::LDO + cc] = Elem<T>::from_float(acc[i][j][v]);
+      }
+  __syncthreads();
+  for (int c = tid; c < BM * CH; c += THREADS) {
+    const int r = c / CH, cc = (c % CH) * VEC;
+    const int m = m0 + r, n = n0 + cc;
+    if (m >= a.M || n >= nseg) continue;
+    store_chunk(m, n, *reinterpret_cast<const uint4*>(sO + r * C::LDO + cc));
   }
 }
 
@@ -224,6 +279,42 @@ static hipError_t launch_proj(const ProjArgs& args, hipStream_t s) {
   const int mt = (a.M + BM - 1) / BM;
   const int nt = a.tiles_seg[0] + a.tiles_seg[1] + a.tiles_seg[2];
   hipLaunchKernelGGL(proj_kernel<T>, dim3(mt, nt), dim3(ProjCfg<T>::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+// One thread per (row m = b*T + t, pair i): the rotary (cos, sin) at position past_len[b] + t.
+struct RopeTableArgs {
+  int32_t B, T, d;
+  double theta;
+  float2* cs;
+  int32_t past_len[kMaxBatch];
+};
+
+__global__ __launch_bounds__(256) void rope_table_kernel(const RopeTableArgs a) {
+  const int half = a.d / 2;
+  const long long n = (long long)a.B * a.T * half;
+  for (long long k = (long long)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (long long)gridDim.x * blockDim.x) {
+    const int i = (int)(k % half);
+    const long long m = k / half;
+    const int b = (int)(m / a.T), t = (int)(m - (long long)b * a.T);
+    double c, sn;
+    rope_angle_cs(a.past_len[b] + t, i, a.d, a.theta, c, sn);
+    a.cs[k] = make_float2((float)c, (float)sn);
+  }
+}
+
+hipError_t launch_rope_table(const int32_t* past_len, int B, int T, int d, double theta, float2* cs,
+                             hipStream_t s) {
+  RopeTableArgs a;
+  a.B = B;
+  a.T = T;
+  a.d = d;
+  a.theta = theta;
+  a.cs = cs;
+  for (int b = 0; b < B && b < kMaxBatch; ++b) a.past_len[b] = past_len[b];
+  const long long n = (long long)B * T * (d / 2);
+  const int grid = (int)std::min<long long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,9 +1,9 @@
 """A stack of decoder layers for the decode step, each layer with its own host KV cache.
 
 Per layer (pre-norm block): h <- h + attn(rmsnorm(h)) Woᵀ, h <- h + swiglu(rmsnorm(h) W_guᵀ) W_downᵀ,
-where attn is the library's host-KV attention layer step (q/k/v projection, append of the new
-token's K/V to the host cache, causal GQA attention over it) and the rest are the library's
-decode-loop kernels. This module only sequences the C-ABI calls and owns the scratch buffers;
+where attn is the library's host-KV attention layer step (q/k/v projection, rotary embedding of q
+and k when rope_theta > 0, append of the new token's K/V to the host cache, causal GQA attention
+over it) and the rest are the library's decode-loop kernels. This module only sequences the C-ABI calls and owns the scratch buffers;
 every step runs in the library's HIP kernels.
 """
 from __future__ import annotations
@@ -21,11 +21,13 @@ class DecodeStack:
     norm weights g_attn, g_mlp [D]. `caches`: one HostKVCache per layer (same batch, heads,
     head_dim and dtype)."""
 
-    def __init__(self, layers: List[Dict], caches: Sequence[HostKVCache], n_q_heads: int, eps: float = 1e-5):
+    def __init__(self, layers: List[Dict], caches: Sequence[HostKVCache], n_q_heads: int, eps: float = 1e-5,
+                 rope_theta: float = 0.0):
         import torch
         if len(layers) != len(caches) or not layers:
             raise ValueError("one cache per layer, at least one layer")
         self.layers, self.caches, self.Hq, self.eps = layers, list(caches), n_q_heads, eps
+        self.rope_theta = rope_theta   # rotary base for q and k (0: none, the layer as the pages give it)
         c = self.caches[0]
         self.B, self.d = c.batch, c.head_dim
         w0 = layers[0]
@@ -46,7 +48,8 @@ class DecodeStack:
         past = np.asarray(past_len, dtype=np.int32)
         for lw, cache in zip(self.layers, self.caches):
             rmsnorm(h, lw["g_attn"], self.a, self.eps)
-            attn_decode(cache, self.a, lw["wq"], lw["wk"], lw["wv"], past, self.Hq, self.o, self.ws)
+            attn_decode(cache, self.a, lw["wq"], lw["wk"], lw["wv"], past, self.Hq, self.o, self.ws,
+                        rope_theta=self.rope_theta)
             linear(self.o, lw["wo"], h, residual=h)
             rmsnorm(h, lw["g_mlp"], self.a, self.eps)
             linear(self.a, lw["w_gu"], self.gu)
