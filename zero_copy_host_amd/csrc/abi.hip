@@ -480,7 +480,10 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   // The projection leaves the new rows in device memory, where attention reads them instead of
   // fetching them back over the link; in the fused path the own-key items write their host copy
   // (the storer role, beside their compute), the baselines write it from the projection epilogue.
-  pa.host_out = !fused;
+  // A step of few rows is the exception: its few own-key items would each push a large share of
+  // the rows over the link, so the projection's many small workgroups write them instead.
+  const bool few_rows = (long long)batch * T <= kProjSmallRows;
+  pa.host_out = !fused || few_rows;
   pa.table = pg.table;
   pa.max_pages = pg.max_pages;
   if (rope > 0.0) {
@@ -518,7 +521,7 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   aa.xcd_group = variant != DKV_PREFILL_NAIVE && P >= 8 && xcd_placement();
   aa.new_from_host = separate;
   aa.fetchers = prefill_fetchers();
-  aa.store_new = fused;
+  aa.store_new = fused && !few_rows;
   for (int b = 0; b < batch; ++b) aa.past_len[b] = past_len[b];
   // With a multiple of 8 pairs, the pairs go in groups of 8, one pair per XCD: each XCD's L2
   // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which

@@ -12,6 +12,7 @@ namespace dkv {
 constexpr int kMaxBatch = 256;   // sequences per call (lengths travel in kernel arguments)
 constexpr int kMaxD = 8192;      // model width held in LDS by the decode kernel
 constexpr int kPageTokens = 16;  // token rows per page of a paged host cache
+constexpr int kProjSmallRows = 256;   // projections of at most this many token rows take the small-tile kernel
 constexpr int kPagedDecodeChunk = 8192;  // keys per decode split at most, paged caches
 constexpr int kPagedSuperchunk = 16384;  // keys per prefill launch at most, paged caches
 constexpr int kWave = 64;

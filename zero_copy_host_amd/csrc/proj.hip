@@ -62,6 +62,27 @@ struct ProjCfg {
   static constexpr int MIN_WAVES = (EB == 2 && DKV_PROJ_MB * DKV_PROJ_NB <= 8) ? 2 : 1;
 };
 
+// Write 16 bytes of output row m, columns [n, n + 16 bytes) of segment seg: Q to device memory,
+// K and V to their host cache rows [past_len[b] + t] and/or the device copies of the new rows.
+template <typename T>
+__device__ inline void proj_store(const ProjArgs& a, const int seg, const int nseg, const int m, const int n,
+                                  const uint4 val) {
+  if (seg == 0) {
+    *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.q_out) + (size_t)m * nseg + n) = val;
+    return;
+  }
+  const int b = m / a.T, t = m - b * a.T;
+  const int gg = n / a.d, i = n - gg * a.d;
+  const size_t bgk = (size_t)b * a.Hkv + gg;
+  if (a.host_out) {
+    T* cache = reinterpret_cast<T*>(seg == 1 ? a.kc : a.vc);
+    const size_t row = host_row(a.table, a.max_pages, b, gg, a.Hkv, a.cap, a.past_len[b] + t);
+    *reinterpret_cast<uint4*>(cache + row * a.d + i) = val;
+  }
+  void* dev = seg == 1 ? a.k_dev : a.v_dev;
+  if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
+}
+
 // 16-bit types with the default tiles: one 256x256 workgroup of 8 waves per CU, two waves per
 // SIMD (256 registers a lane). Against two 128x256 workgroups per CU it loads a third fewer
 // operand bytes per MFMA into the CU.
@@ -185,20 +206,7 @@ void proj_kernel(const ProjArgs a) {
   // ---- epilogue: round to T into an LDS tile, then write whole rows (16 bytes a lane)
   constexpr int CH = BN / VEC;                   // 16-byte chunks per output row
   auto store_chunk = [&](const int m, const int n, const uint4 val) __attribute__((always_inline)) {
-    if (seg == 0) {
-      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.q_out) + (size_t)m * nseg + n) = val;
-    } else {
-      const int b = m / a.T, t = m - b * a.T;
-      const int gg = n / a.d, i = n - gg * a.d;
-      const size_t bgk = (size_t)b * a.Hkv + gg;
-      if (a.host_out) {
-        T* cache = reinterpret_cast<T*>(seg == 1 ? a.kc : a.vc);
-        const size_t row = host_row(a.table, a.max_pages, b, gg, a.Hkv, a.cap, a.past_len[b] + t);
-        *reinterpret_cast<uint4*>(cache + row * a.d + i) = val;
-      }
-      void* dev = seg == 1 ? a.k_dev : a.v_dev;
-      if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
-    }
+    proj_store<T>(a, seg, nseg, m, n, val);
   };
 
   if (a.rope_cs != nullptr && seg < 2) {
@@ -271,10 +279,116 @@ void proj_kernel(const ProjArgs a) {
   }
 }
 
+// ---- few rows (M <= kProjSmallRows): the 256x256 tiles would leave most CUs idle (a 128-token step has
+// one row of tiles), so each workgroup takes 32 rows x one head (d columns) of a segment and its
+// 8 waves split the reduction: wave w takes reduction steps w, w + 8, ... and the partial tiles
+// are summed in LDS in wave order. Operands come straight from L2 into MFMA fragments (no LDS
+// staging: the matrices are small and every element is read by few workgroups). fp32 takes its
+// fragments as 16-byte loads too: with the 32x32x2 instruction, lanes 0-31 supply reduction
+// index 8j + s and lanes 32-63 index 8j + 4 + s for s = 0..3 (any order of the reduction index
+// is the same sum, the same for both operands), so four instructions consume one load.
+constexpr int kSmallWaves = 8;
+
+template <typename T, int DH>
+__global__ __launch_bounds__(64 * kSmallWaves) void proj_small_kernel(const ProjArgs a) {
+  constexpr int EB = sizeof(T), VEC = 16 / EB;
+  constexpr int NB = DH / 32;                         // 32-column blocks of the head
+  constexpr int STEP = EB == 2 ? 16 : 8;              // reduction elements per step
+  constexpr int LDR = DH + 4;                         // padded fp32 row of the partial tiles
+  __shared__ __attribute__((aligned(16))) float sR[kSmallWaves * 32 * LDR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  constexpr int order[3] = {1, 2, 0};                 // K and V first (their rows go to the host)
+  int oi = 0, ty = blockIdx.y;
+  while (oi < 2 && ty >= a.tiles_seg[order[oi]]) { ty -= a.tiles_seg[order[oi]]; ++oi; }
+  const int seg = order[oi];
+  const int nseg = a.n_seg[seg];
+  const int n0 = ty * DH, m0 = blockIdx.x * 32;
+  const int D = a.D;
+  const T* __restrict__ X = reinterpret_cast<const T*>(a.x) + (size_t)min(m0 + (lane & 31), a.M - 1) * D;
+  const T* __restrict__ W = reinterpret_cast<const T*>(a.w[seg]) + (size_t)(n0 + (lane & 31)) * D;
+  const int koff = (lane >> 5) * (STEP / 2);
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+  const int nsteps = D / STEP;
+  for (int st = wave; st < nsteps; st += kSmallWaves) {
+    const int k = st * STEP + koff;
+    const uint4 xa = *reinterpret_cast<const uint4*>(X + k);
+    uint4 wb[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wb[j] = *reinterpret_cast<const uint4*>(W + (size_t)j * 32 * D + k);
+    if constexpr (EB == 2) {
+      typedef typename Mfma<T>::frag F;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] = Mfma<T>::mma(__builtin_bit_cast(F, xa), __builtin_bit_cast(F, wb[j]), acc[j]);
+    } else {
+      const float* fa = reinterpret_cast<const float*>(&xa);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const float* fb = reinterpret_cast<const float*>(&wb[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j] = Mfma<float>::mma(fa[e], fb[e], acc[j]);
+      }
+    }
+  }
+  // partial tiles to LDS, then the sum over waves in wave order
+  float* mine = sR + wave * 32 * LDR;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mine[acc_row(v, lane) * LDR + j * 32 + (lane & 31)] = acc[j][v];
+  __syncthreads();
+  for (int e = tid; e < 32 * DH; e += 64 * kSmallWaves) {
+    const int r = e / DH, c = e - r * DH;
+    float sum = sR[r * LDR + c];
+#pragma unroll
+    for (int w = 1; w < kSmallWaves; ++w) sum += sR[w * 32 * LDR + r * LDR + c];
+    sR[r * LDR + c] = sum;
+  }
+  __syncthreads();
+  // round (after the rotary embedding of Q and K, if any) and store 16-byte chunks
+  const bool rope = a.rope_cs != nullptr && seg < 2;
+  constexpr int HALF = DH / 2;
+  for (int c = tid; c < 32 * (DH / VEC); c += 64 * kSmallWaves) {
+    const int r = c / (DH / VEC), cc = (c % (DH / VEC)) * VEC;
+    const int m = m0 + r;
+    if (m >= a.M) continue;
+    const float* own = sR + r * LDR + cc;
+    T res[VEC];
+    if (rope) {
+      const bool low = cc < HALF;
+      const float* oth = sR + r * LDR + (low ? cc + HALF : cc - HALF);
+      const float2* cs = a.rope_cs + (size_t)m * HALF + (low ? cc : cc - HALF);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float2 w = cs[e];
+        res[e] = Elem<T>::from_float(low ? own[e] * w.x - oth[e] * w.y : own[e] * w.x + oth[e] * w.y);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) res[e] = Elem<T>::from_float(own[e]);
+    }
+    uint4 val;
+    __builtin_memcpy(&val, res, 16);
+    proj_store<T>(a, seg, nseg, m, n0 + cc, val);
+  }
+}
+
 template <typename T>
 static hipError_t launch_proj(const ProjArgs& args, hipStream_t s) {
-  constexpr int BM = ProjCfg<T>::BM, BN = ProjCfg<T>::BN;
   ProjArgs a = args;
+  if (a.M <= kProjSmallRows) {
+    for (int g = 0; g < 3; ++g) a.tiles_seg[g] = a.n_seg[g] / a.d;
+    const dim3 grid((a.M + 31) / 32, a.tiles_seg[0] + a.tiles_seg[1] + a.tiles_seg[2]);
+    if (a.d == 128) hipLaunchKernelGGL((proj_small_kernel<T, 128>), grid, dim3(64 * kSmallWaves), 0, s, a);
+    else hipLaunchKernelGGL((proj_small_kernel<T, 64>), grid, dim3(64 * kSmallWaves), 0, s, a);
+    return hipGetLastError();
+  }
+  constexpr int BM = ProjCfg<T>::BM, BN = ProjCfg<T>::BN;
   for (int g = 0; g < 3; ++g) a.tiles_seg[g] = (a.n_seg[g] + BN - 1) / BN;
   const int mt = (a.M + BM - 1) / BM;
   const int nt = a.tiles_seg[0] + a.tiles_seg[1] + a.tiles_seg[2];
