@@ -101,16 +101,22 @@ def cpu_model():
 
 
 def _oracle_threads():
-    import threadpoolctl
-    return max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    """Threads for the C oracle: the host cores this process may use, at most 16 (a one-GPU machine's
+    share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def cpu_baseline_prefill(name, n_tokens=128):
     """The oracle, as it is, on a bounded sample of workload `name`'s prefill step: the first
-    n_tokens of the step's new tokens (every sequence, every head), on the same past keys. Its
-    rate is the sample's tokens over the oracle's time; later tokens of the full step see up to
-    T more keys, so the full step would run slower per token."""
-    import oracle
+    n_tokens of the step's new tokens (every sequence, every head), on the same past keys, timed
+    in the oracle's threaded C form (fp64 loops over (sequence, kv head, block of query tokens)).
+    Its rate is the sample's tokens over the oracle's time; later tokens of the full step see up
+    to T more keys, so the full step would run slower per token."""
+    from oracle import cref
     import synth
     w = synth.workload(name)
     dr = synth.Draw(w.seed)
@@ -121,20 +127,24 @@ def cpu_baseline_prefill(name, n_tokens=128):
     kc = np.zeros((w.B, w.Hkv, cap, w.d), dtype=np.float32)
     vc = np.zeros_like(kc)
     synth.fill_past(dr, kc, vc, past, w.dtype)
+    threads = _oracle_threads()
+    cref.lib()
     t0 = time.perf_counter()
-    oracle.layer_step(x, wq, wk, wv, kc, vc, past, w.Hq, w.dtype)
+    cref.layer_step(x, wq, wk, wv, kc, vc, past, w.Hq, w.dtype, threads=threads)
     el = time.perf_counter() - t0
     tok = w.B * n_tokens
-    return {"value": tok / el, "unit": "prefill tok/s per layer", "cores": int(_oracle_threads()), "kind": "oracle",
+    return {"value": tok / el, "unit": "prefill tok/s per layer", "cores": threads, "kind": "oracle",
             "seconds": el, "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"the first {n_tokens} of the {w.T} new tokens of each of the {w.B} sequences of {name} "
                       f"(projection, append, causal attention over {int(past[0])}+ keys, all {w.Hq} heads), "
-                      f"numpy fp64 oracle; the full step's later tokens see up to {w.T} more keys each"}
+                      f"fp64 C oracle on {threads} threads; the full step's later tokens see up to {w.T} more "
+                      f"keys each"}
 
 
 def cpu_baseline_decode(name, min_seconds=10.0):
-    """The oracle, as it is, on whole decode steps of workload `name`, repeated for ~min_seconds."""
-    import oracle
+    """The oracle, as it is, on whole decode steps of workload `name`, repeated for ~min_seconds,
+    in its threaded C form."""
+    from oracle import cref
     import synth
     w = synth.workload(name)
     dr = synth.Draw(w.seed)
@@ -144,18 +154,20 @@ def cpu_baseline_decode(name, min_seconds=10.0):
     kc = np.zeros((w.B, w.Hkv, w.cap, w.d), dtype=np.float32)
     vc = np.zeros_like(kc)
     synth.fill_past(dr, kc, vc, past, w.dtype)
+    threads = _oracle_threads()
+    cref.lib()
     t0 = time.perf_counter()
     n = 0
     while True:
-        oracle.layer_step(x, wq, wk, wv, kc, vc, past, w.Hq, w.dtype)
+        cref.layer_step(x, wq, wk, wv, kc, vc, past, w.Hq, w.dtype, threads=threads)
         n += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    return {"value": el / n * 1e6, "unit": "us per layer decode step", "cores": int(_oracle_threads()),
+    return {"value": el / n * 1e6, "unit": "us per layer decode step", "cores": threads,
             "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{n} full decode step(s) of {name} (all {w.B} sequences, {int(past[0]) + 1} keys each), "
-                      f"numpy fp64 oracle"}
+                      f"fp64 C oracle on {threads} threads"}
 
 
 def read_counter_summary(name, kernel_src_hash):

@@ -2,7 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links this
 package; only the tests, the package's smoke check and the benchmark's CPU-baseline
-leg use it. It shares no code with the HIP library.
+leg use it. It shares no code with the HIP library. The same layer step (without the
+rotary embedding) is also written as plain threaded C loops in layer_ref.c (bound by
+oracle.cref): the form the CPU baseline times, pinned against this one and the brute force.
 
 What it computes (the plain definition; the method reaches the same result, only with a
 different memory layout and transfer schedule — "DirectKV Guide: Zero-Copy KV

@@ -104,3 +104,11 @@ def test_counters_summary_means_per_dispatch(tmp_path, capsys):
     out = json.loads(capsys.readouterr().out)
     assert out["kA"]["dispatches"] == 2 and out["kA"]["FETCH_SIZE"] == pytest.approx(30.0)
     assert out["kB"]["WRITE_SIZE"] == pytest.approx(4.0)
+
+
+def test_cpu_baseline_uses_the_threaded_c_oracle():
+    import bench
+    r = bench.cpu_baseline_prefill("tiny_f32_prefill128_decode1", n_tokens=8)
+    assert r["kind"] == "oracle" and r["unit"] == "prefill tok/s per layer"
+    assert r["cores"] == bench._oracle_threads() >= 1
+    assert r["value"] > 0 and "C oracle" in r["sample"] and r["cpu_model"]
