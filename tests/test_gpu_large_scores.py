@@ -37,6 +37,10 @@ PREFILL = [
     (1, 130, [3000], 256, 8, 8, 64, "f32", 1024),        # G = 1, fp32
     (1, 97, [2100], 256, 8, 2, 128, "f32", 512),         # G = 4, fp32, d = 128
     (3, 64, [0, 700, 4100], 256, 8, 2, 128, "bf16", 1024),   # ragged, one empty past
+    # one query tile per pair: the keys are split over workgroups and the states merged
+    (1, 16, [7000], 256, 16, 2, 128, "bf16", None),
+    (2, 32, [3000, 9000], 256, 8, 2, 128, "f16", None),
+    (1, 40, [2500], 256, 4, 4, 64, "f32", None),
 ]
 
 

@@ -182,6 +182,29 @@ def test_paged_prefill_equals_contiguous_bitwise(chunk, monkeypatch):
     compare(out_p, ref, "bf16", f"paged prefill chunk={chunk}")
 
 
+def test_paged_key_split_prefill_equals_contiguous_bitwise():
+    """One query tile per pair, so the keys are split over workgroups; a past of 20000 keys is
+    longer than one paged launch may stage, so the splits are also bounded by that."""
+    case = _case(303, 2, 16, [20000, 5000], 256, 8, 2, 128, "bf16")
+    x, past = case["x"], case["past_len"]
+    out_c, kc_bits, vc_bits = _contiguous(case, lambda g: g.prefill(x, past))
+    pl = PagedLayer(case, seed=3)
+    try:
+        out_p = pl.prefill(x, past)
+        n = int(max(past)) + case["T"]
+        kp_bits, vp_bits = pl.logical_bits(pl.cache.k, n), pl.logical_bits(pl.cache.v, n)
+        _check_untouched(pl, past, case["T"])
+    finally:
+        pl.free()
+    assert np.array_equal(out_p, out_c), "paged prefill differs from contiguous prefill"
+    for b in range(case["B"]):
+        m = int(past[b]) + case["T"]
+        assert np.array_equal(kp_bits[b, :, :m], kc_bits[b, :, :m])
+        assert np.array_equal(vp_bits[b, :, :m], vc_bits[b, :, :m])
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    compare(out_p, oracle_step(case, x, past, kc, vc), "bf16", "paged prefill with key splits")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_paged_append_equals_contiguous_bitwise(dtype):
     case = _case(303, 3, 37, [5, 0, 130], 256, 4, 2, 64, dtype)

@@ -303,6 +303,42 @@ def test_tiny_layer_prefill_then_decode():
     compare(out_d, ref_d, "f32", "tiny decode")
 
 
+def test_prefill_key_splits_ragged_with_empty_splits():
+    """One query tile per pair (T * G <= 256): each pair's keys are split over workgroups and a
+    second launch merges the splits. With a long and an empty past in one call, the short pair
+    has fewer key tiles than splits, so most of its splits (the first among them) see no keys."""
+    case = _case(21, 3, 16, [0, 9000, 130], 256, 16, 2, 128, "bf16")
+    out, ref, kg, vg, kc, vc = _run_prefill(case, canary=True)
+    compare(out, ref, "bf16", "prefill with key splits")
+    ak = absdot_rows(case["x"], case["wk"], case["Hkv"], case["d"])
+    av = absdot_rows(case["x"], case["wv"], case["Hkv"], case["d"])
+    for b in range(case["B"]):
+        L = int(case["past_len"][b])
+        compare_rows(kg[b, :, L:L + 16], kc[b, :, L:L + 16], "bf16", ak[b], case["D"], "new K rows")
+        compare_rows(vg[b, :, L:L + 16], vc[b, :, L:L + 16], "bf16", av[b], case["D"], "new V rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_token_prefill_matches_decode(dtype):
+    """A prefill of one token (key splits over the whole cache) against the decode step on the
+    same inputs and the oracle."""
+    case = _case(22, 2, 1, [5000, 777], 256, 8, 2, 128, dtype)
+    g = GpuLayer(case)
+    try:
+        p = g.prefill(case["x"], case["past_len"])
+    finally:
+        g.free()
+    g = GpuLayer(case)
+    try:
+        dcd = g.decode(case["x"], case["past_len"])
+    finally:
+        g.free()
+    kc, vc = case["kp"].copy(), case["vp"].copy()
+    ref = oracle_step(case, case["x"], case["past_len"], kc, vc)
+    compare(p, ref, dtype, "one-token prefill")
+    compare(dcd, ref, dtype, "decode")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_prefill_causal_perturbation_is_bitwise():

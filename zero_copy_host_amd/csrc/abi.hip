@@ -267,7 +267,7 @@ bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, i
 
 // ---- prefill workspace layout
 struct PrefillWs {
-  size_t q, k_new, v_new, state, nstate, rope, total;
+  size_t q, k_new, v_new, state, nstate, rope, split, total;
 };
 
 PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
@@ -281,7 +281,10 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   const size_t sb = round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, std::max(1, G)), 256);
   w.nstate = w.state + sb;
   w.rope = w.nstate + sb;   // rotary (cos, sin) table of the call's rows (attn_prefill_rope)
-  w.total = w.rope + round_up((size_t)batch * T * (d / 2) * 2 * sizeof(float), 256);
+  w.split = w.rope + round_up((size_t)batch * T * (d / 2) * 2 * sizeof(float), 256);
+  // one query tile per pair: the running states of up to kMaxKeySplits key splits per pair
+  const bool one_tile = (long long)T * std::max(1, G) <= attn_rows_per_tile();
+  w.total = w.split + (one_tile ? kMaxKeySplits * sb : 0);
   return w;
 }
 
@@ -475,6 +478,23 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
 
   const bool separate = variant == DKV_PREFILL_SEPARATE;
   const bool fused = variant == DKV_PREFILL_FUSED;
+  const int rows = attn_rows_per_tile();
+  const int Q = (T * G + rows - 1) / rows;
+  const int P = batch * c->n_kv_heads;
+  // Key splits: with one query tile per pair no key is shared between query tiles, so instead of
+  // super-chunk launches each pair's keys are split over enough workgroups to fill the chip (two
+  // per CU), and a second launch merges the splits' states.
+  int n_splits = 0;
+  if (fused && Q == 1) {
+    int max_keys = 0;
+    for (int b = 0; b < batch; ++b) max_keys = std::max(max_keys, past_len[b] + T);
+    const int kt = attn_key_tile(c->dtype, c->head_dim);
+    const int tiles = (max_keys + kt - 1) / kt;
+    n_splits = std::min({kMaxKeySplits, tiles, std::max(1, (2 * cu_count() + P - 1) / P)});
+    // a paged launch stages its keys' page ids in LDS: a split holds at most kPagedSuperchunk keys
+    if (paged) n_splits = std::max(n_splits, (tiles + kPagedSuperchunk / kt - 1) / (kPagedSuperchunk / kt));
+    if (n_splits <= 1 || n_splits > kMaxKeySplits) n_splits = 0;
+  }
   ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
                           separate ? nullptr : vn);
   // The projection leaves the new rows in device memory, where attention reads them instead of
@@ -482,8 +502,9 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   // (the storer role, beside their compute), the baselines write it from the projection epilogue.
   // A step of few rows is the exception: its few own-key items would each push a large share of
   // the rows over the link, so the projection's many small workgroups write them instead.
+  // With key splits, storer workgroups of the split launch write them while the splits compute.
   const bool few_rows = (long long)batch * T <= kProjSmallRows;
-  pa.host_out = !fused || few_rows;
+  pa.host_out = !fused || (few_rows && n_splits == 0);
   pa.table = pg.table;
   pa.max_pages = pg.max_pages;
   if (rope > 0.0) {
@@ -514,14 +535,11 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
   aa.cap = c->capacity;
   aa.table = pg.table;
   aa.max_pages = pg.max_pages;
-  const int rows = attn_rows_per_tile();
-  const int Q = (T * G + rows - 1) / rows;
   aa.q_tiles = Q;
-  const int P = batch * c->n_kv_heads;
   aa.xcd_group = variant != DKV_PREFILL_NAIVE && P >= 8 && xcd_placement();
   aa.new_from_host = separate;
   aa.fetchers = prefill_fetchers();
-  aa.store_new = fused && !few_rows;
+  aa.store_new = fused && !few_rows && n_splits == 0;
   for (int b = 0; b < batch; ++b) aa.past_len[b] = past_len[b];
   // With a multiple of 8 pairs, the pairs go in groups of 8, one pair per XCD: each XCD's L2
   // then holds one pair's super-chunk, twice as many keys as when two pairs share it, which
@@ -534,6 +552,25 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
     ++n_attn;
     return le == hipSuccess ? DKV_OK : hip_fail(le, "attention launch");
   };
+  if (n_splits > 0) {
+    aa.n_splits = n_splits;
+    aa.split_stride = (int64_t)(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, G) / sizeof(float));
+    aa.state = reinterpret_cast<float*>(w + lay.split);
+    aa.pair0 = 0;
+    aa.pairs = P;
+    aa.xcd_group = 0;
+    aa.split_combine = 0;
+    // storers: about 16 KB of new rows each (4 KB to 16 KB measure the same), at most one per CU
+    const size_t new_bytes = (size_t)2 * P * T * c->head_dim * elem_size(c->dtype);
+    aa.split_storers = (int)std::min<size_t>((size_t)cu_count(), std::max<size_t>(1, (new_bytes + 16383) / 16384));
+    aa.store_new = 1;
+    int st = launch();
+    if (st) return st;
+    aa.split_combine = 1;
+    if ((st = launch())) return st;
+    ta.done(n_attn);
+    return DKV_OK;
+  }
   for (int pair0 = 0; pair0 < P; pair0 += group) {
     aa.pair0 = pair0;
     aa.pairs = group;

@@ -155,7 +155,8 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   const int key_hi = min(it.kc1, L + rlast / G + 1);  // keys any row here may see, exclusive
   const int key_lo = it.kc0;
   const bool work = key_lo < key_hi;
-  if (!work && !it.last) return;                 // nothing visible and nothing to finalise
+  // nothing visible and nothing to finalise (a key split still leaves its empty state)
+  if (!work && !it.last && !a.n_splits) return;
   const int key_all = L + row0 / G + 1;          // keys below this are visible to every row
 
   const int r = row0 + wave * 32 + col;          // this lane's query row
@@ -385,7 +386,12 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
     // tile i computes from LDS buffer i % 2; register set 0 carries tiles 1, 3, 5, ... and set 1
     // tiles 2, 4, 6, ... (loaded two tiles ahead, stored to LDS one tile ahead)
     Scores sc;
+    // A wave skips the products of a tile none of its rows can see: a 32-row block past the
+    // pair's rows (the last query tile of a pair is often part-filled) or keys all later than its
+    // last row. Such a tile would add exact zeros, so skipping it changes no bit.
+    const int wave_keys = wvalid ? L + (min(row0 + wave * 32 + 31, nrows - 1)) / G + 1 : 0;   // exclusive
     auto tile = [&](const int j0, const int buf) __attribute__((always_inline)) {
+      if (j0 >= wave_keys) return;
       qk(sK[buf], sc);
       rebase(j0, sc, std::true_type{});
       probs(sc, pb);
@@ -450,10 +456,12 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
       auto half_lean = [&](const int i, const int buf, const int set) __attribute__((always_inline)) {
         sstore_lean(1 - buf, set);
         gload_lean(set, tj(i + 3));
-        qk(sK[buf], sc);
-        rebase(tj(i), sc, std::false_type{});
-        probs(sc, pb);
-        pv(sV[buf], pb);
+        if (wvalid) {
+          qk(sK[buf], sc);
+          rebase(tj(i), sc, std::false_type{});
+          probs(sc, pb);
+          pv(sV[buf], pb);
+        }
         __syncthreads();
       };
       for (; i < n_lean; i += 2) {
@@ -469,6 +477,31 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   }
 
   if (it.last) {
+    if (a.n_splits && wvalid) {
+      // key-split mode: fold in the states of splits 1 .. n_splits - 1 (this item read split 0's).
+      // A split whose keys this row cannot see left m = -inf and is skipped; split 0 starts at key
+      // 0, which every row sees, unless it is empty (fewer key tiles than splits): then the first
+      // split with keys is taken as it is.
+      for (int j = 1; j < a.n_splits; ++j) {
+        const float* ns = it.state + (size_t)j * a.split_stride + st_off;
+        const float m2 = __builtin_nontemporal_load(ns + DB * 16 * 64 + lane);
+        if (m2 == -INFINITY) continue;
+        const float l2 = __builtin_nontemporal_load(ns + (DB * 16 + 1) * 64 + lane);
+        const bool have = m_run != -INFINITY;
+        const float M = have ? fmaxf(m_run, m2) : m2;
+        const float a1 = have ? __builtin_amdgcn_exp2f(m_run - M) : 0.f;
+        const float a2 = __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float o2 = __builtin_nontemporal_load(ns + (db * 16 + v) * 64 + lane);
+            o[db][v] = have ? fmaf(o[db][v], a1, o2 * a2) : o2;
+          }
+        l_run = have ? fmaf(l_run, a1, l2 * a2) : l2;
+        m_run = M;
+      }
+    }
     if (it.merge && wvalid) {
       // fold in the state of this step's own keys: O = (o 2^(m - M) + o' 2^(m' - M)) / (l 2^(m - M) +
       // l' 2^(m' - M)), M = max(m, m'); a sequence with no past keys has only the latter
@@ -520,10 +553,47 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
 // With at least 8 pairs, pair p is served only by XCD p % 8 (workgroup i runs on XCD i % 8).
 // The second bound is the minimum number of waves per SIMD: two, 256 VGPRs a lane. (Four waves
 // per SIMD would leave 128, under what the three kinds of item need at d = 64.)
+//
+// Key-split mode (a.n_splits > 0; the pairs have one query tile each, so no key is shared between
+// query tiles and nothing is gained by keeping a super-chunk in L2): workgroup i takes pair
+// i % pairs and key split i / pairs, an equal share of the pair's key tiles (past and own keys),
+// and leaves its running state in that split's state array; a.split_storers more workgroups
+// write this step's new rows to the host cache meanwhile (the storer role). A second launch
+// (a.split_combine) folds the splits' states together per pair and writes the output.
 template <typename T, int DH, int G, bool PAGED>
 __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWAVES)
 void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds<T, DH, PAGED> lds;
+  if (a.n_splits) {
+    if (!a.split_combine && (int)blockIdx.x >= a.pairs * a.n_splits) {
+      // storer workgroup s: an equal share of the (pair, token) rows of this step, K and V, from
+      // the device copies to the host cache, while the split items compute
+      const int s = (int)blockIdx.x - a.pairs * a.n_splits;
+      const int rows = a.pairs * a.T;
+      const int r0 = (int)((long long)rows * s / a.split_storers);
+      const int r1 = (int)((long long)rows * (s + 1) / a.split_storers);
+      for (int row = r0; row < r1;) {   // runs of one pair's consecutive tokens
+        const int pp = row / a.T, t0 = row - pp * a.T;
+        const int t1 = min(a.T, t0 + (r1 - row));
+        attn_store<T, DH, PAGED>(a, a.pair0 + pp, t0, t1);
+        row += t1 - t0;
+      }
+      return;
+    }
+    const int p = a.pair0 + (int)blockIdx.x % a.pairs;
+    if (a.split_combine) {
+      attn_item<T, DH, G, PAGED>(a, AttnItem{p, 0, 0, 0, 0, 1, 0, a.state}, lds);
+    } else {
+      constexpr int KT = AttnCfg<T, DH>::KT;
+      const int j = (int)blockIdx.x / a.pairs;
+      const int nk = a.past_len[p / a.Hkv] + a.T;                 // the pair's keys, past and own
+      const int tiles = (nk + KT - 1) / KT;
+      const int t0 = (int)((long long)tiles * j / a.n_splits), t1 = (int)((long long)tiles * (j + 1) / a.n_splits);
+      attn_item<T, DH, G, PAGED>(a, AttnItem{p, 0, t0 * KT, min(t1 * KT, nk), 1, 0, 0, a.state + (size_t)j * a.split_stride},
+                                 lds);
+    }
+    return;
+  }
   const int P = a.pairs;
   int p, r;   // pair, and the item's position in that pair's sequence of items
   if (a.xcd_group) {
@@ -563,8 +633,10 @@ void attn_kernel(const AttnArgs a) {
 template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int P = a.pairs;
-  const int items = (a.past_items ? a.q_tiles : 0) + a.dev_q1 - a.dev_q0;   // per pair
-  const int grid = a.xcd_group ? 8 * ((P + 7) / 8) * items : P * items;
+  const int items = a.n_splits ? (a.split_combine ? 1 : a.n_splits)
+                               : (a.past_items ? a.q_tiles : 0) + a.dev_q1 - a.dev_q0;   // per pair
+  const int grid = a.xcd_group && !a.n_splits ? 8 * ((P + 7) / 8) * items
+                                              : P * items + (a.n_splits && !a.split_combine ? a.split_storers : 0);
   hipLaunchKernelGGL((attn_kernel<T, DH, G, PAGED>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
   return hipGetLastError();
 }
@@ -597,6 +669,11 @@ attn_fn find_attn(int dtype, int d, int G, bool paged) {
 }
 
 int attn_rows_per_tile() { return 32 * DKV_ATTN_WAVES; }
+
+int attn_key_tile(int dtype, int d) {
+  if (dtype == 0) return d == 128 ? AttnCfg<float, 128>::KT : AttnCfg<float, 64>::KT;
+  return d == 128 ? AttnCfg<__bf16, 128>::KT : AttnCfg<__bf16, 64>::KT;
+}
 
 size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G) {
   const size_t nblk = ((size_t)T * G + 31) / 32;

@@ -12,7 +12,8 @@ namespace dkv {
 constexpr int kMaxBatch = 256;   // sequences per call (lengths travel in kernel arguments)
 constexpr int kMaxD = 8192;      // model width held in LDS by the decode kernel
 constexpr int kPageTokens = 16;  // token rows per page of a paged host cache
-constexpr int kProjSmallRows = 256;   // projections of at most this many token rows take the small-tile kernel
+constexpr int kProjSmallRows = 256;
+constexpr int kMaxKeySplits = 32;     // key splits per pair at most, prefills of one query tile per pair   // projections of at most this many token rows take the small-tile kernel
 constexpr int kPagedDecodeChunk = 8192;  // keys per decode split at most, paged caches
 constexpr int kPagedSuperchunk = 16384;  // keys per prefill launch at most, paged caches
 constexpr int kWave = 64;
@@ -225,6 +226,11 @@ struct AttnArgs {
   int32_t dev_final;        // 1: own-key items finalise the output (no past keys anywhere)
   int32_t merge_new;        // 1: finalising past-key items fold in nstate
   int32_t store_new;        // 1: own-key items write their tokens' new rows to the host cache
+  int32_t n_splits;         // key-split mode (one query tile per pair): key splits per pair; 0 = off
+  int32_t split_combine;    // key-split mode: 0 = the split items, 1 = the items merging their states
+  int64_t split_stride;     // key-split mode: floats between two splits' state arrays (from `state`)
+  int32_t split_storers;    // key-split mode: workgroups after the split items that copy this step's
+                            // new K/V rows from their device copies to the host cache
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
   int32_t past_len[kMaxBatch];
@@ -247,6 +253,7 @@ attn_fn find_attn(int dtype, int d, int G, bool paged);
 int decode_slots(int dtype, int d);  // key rows one decode WG consumes per step
 int attn_rows_per_tile();            // query rows (token x head) per prefill WG
 size_t attn_state_bytes(int d, int batch, int n_kv_heads, int T, int G);
+int attn_key_tile(int dtype, int d);  // keys per LDS tile of the prefill attention
 
 hipError_t launch_hostlink(void* p, size_t bytes, int mode, int n_wg, hipStream_t s);
 

@@ -314,24 +314,37 @@ __global__ __launch_bounds__(64 * kSmallWaves) void proj_small_kernel(const Proj
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+  // a wave's steps go U at a time: all U steps' loads are issued before their products, so a
+  // short reduction (a few steps per wave) waits for memory once, not once per step
+  constexpr int U = 4;
   const int nsteps = D / STEP;
-  for (int st = wave; st < nsteps; st += kSmallWaves) {
-    const int k = st * STEP + koff;
-    const uint4 xa = *reinterpret_cast<const uint4*>(X + k);
-    uint4 wb[NB];
+  for (int st0 = wave; st0 < nsteps; st0 += U * kSmallWaves) {
+    uint4 xa[U], wb[U][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) wb[j] = *reinterpret_cast<const uint4*>(W + (size_t)j * 32 * D + k);
-    if constexpr (EB == 2) {
-      typedef typename Mfma<T>::frag F;
+    for (int u = 0; u < U; ++u) {
+      const int k = min(st0 + u * kSmallWaves, nsteps - 1) * STEP + koff;   // past the end: reread the last step
+      xa[u] = *reinterpret_cast<const uint4*>(X + k);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[j] = Mfma<T>::mma(__builtin_bit_cast(F, xa), __builtin_bit_cast(F, wb[j]), acc[j]);
-    } else {
-      const float* fa = reinterpret_cast<const float*>(&xa);
+      for (int j = 0; j < NB; ++j) wb[u][j] = *reinterpret_cast<const uint4*>(W + (size_t)j * 32 * D + k);
+    }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const float* fb = reinterpret_cast<const float*>(&wb[j]);
+    for (int u = 0; u < U; ++u) {
+      // a step past the end adds the zero product (exact) instead of branching: a branch here
+      // lets the compiler sink each step's loads down to their use
+      if (st0 + u * kSmallWaves >= nsteps) xa[u] = make_uint4(0, 0, 0, 0);
+      if constexpr (EB == 2) {
+        typedef typename Mfma<T>::frag F;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[j] = Mfma<float>::mma(fa[e], fb[e], acc[j]);
+        for (int j = 0; j < NB; ++j)
+          acc[j] = Mfma<T>::mma(__builtin_bit_cast(F, xa[u]), __builtin_bit_cast(F, wb[u][j]), acc[j]);
+      } else {
+        const float* fa = reinterpret_cast<const float*>(&xa[u]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float* fb = reinterpret_cast<const float*>(&wb[u][j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j] = Mfma<float>::mma(fa[e], fb[e], acc[j]);
+        }
       }
     }
   }
