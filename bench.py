@@ -69,6 +69,19 @@ class EventTimer:
         self.ms = self.s.elapsed_time(self.e)
 
 
+def _timed_phases(dkv, fn, n):
+    """Run fn() n times with the library's per-phase kernel timing on; returns its records."""
+    import torch
+    torch.cuda.synchronize()
+    dkv.timing(True)
+    try:
+        for _ in range(n):
+            fn()
+        return dkv.timing_read()
+    finally:
+        dkv.timing(False)
+
+
 def hostlink_peak(dkv, nbytes=1 << 30, reps=8):
     """Kernel streaming read and write rate of pinned host memory (GB/s): the best of `reps`
     separately timed passes over a 1 GiB buffer (a peak, so one slow pass does not lower it)."""
@@ -327,19 +340,18 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
                      dtype=torch.uint8, device="cuda")
 
     def timed(var, n, nwarm, kernels=False):
+        step = lambda: dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out,
+                                                ws, var)
         for _ in range(nwarm):
-            dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
+            step()
         torch.cuda.synchronize()
-        if kernels:
-            dkv.timing(True)
         with EventTimer() as t:
             for _ in range(n):
-                dkv.attn_prefill_variant(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws, var)
-        kern = None
-        if kernels:
-            tr = dkv.timing_read()
-            dkv.timing(False)
-            kern = {ph: _phase(tr, ph, n) for ph in ("projection", "prefill_attention")}
+                step()
+        # the kernel times come from a second pass of the same steps with the library's timing
+        # events on (their recording costs host time, which would count in a launch-bound step)
+        kern = {ph: _phase(tr, ph, n) for ph in ("projection", "prefill_attention")} if kernels and (
+            tr := _timed_phases(dkv, step, n)) is not None else None
         return t.ms / n, kern
 
     ms, kern = timed(variant, steps, warmup, kernels=True)
@@ -368,13 +380,14 @@ def run_prefill(dkv, name, steps=5, warmup=2, peak_read=None, decode_steps=0, va
         # a single decode step is timed as the mean of 20 runs of that step (same lengths, so
         # each run rewrites the same row); longer runs advance the lengths step by step
         reps = 20 if decode_steps == 1 else 1
-        dkv.timing(True)
-        with EventTimer() as t:
+
+        def steps_once():
             for _ in range(reps):
                 for s_ in range(decode_steps):
                     dkv.attn_decode(cache, xs[s_], dev["wq"], dev["wk"], dev["wv"], past + w.T + s_, w.Hq, outd, wsd)
-        tr = dkv.timing_read()
-        dkv.timing(False)
+        with EventTimer() as t:
+            steps_once()
+        tr = _timed_phases(dkv, steps_once, 1)
         n = decode_steps * reps
         ms = t.ms / n
         mid = past + w.T + decode_steps // 2
@@ -398,12 +411,11 @@ def run_decode(dkv, name, steps=10, warmup=2, peak_read=None):
     for _ in range(warmup):
         dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
     torch.cuda.synchronize()
-    dkv.timing(True)
+    step = lambda: dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
     with EventTimer() as t:
         for _ in range(steps):
-            dkv.attn_decode(cache, dev["x"], dev["wq"], dev["wk"], dev["wv"], past, w.Hq, out, ws)
-    tr = dkv.timing_read()
-    dkv.timing(False)
+            step()
+    tr = _timed_phases(dkv, step, steps)
     cache.free()
     kd = {ph: _phase(tr, ph, steps) for ph in ("decode_qproj", "decode_attention", "decode_combine")}
     return {"workload": name, "steps": steps, "past_len": [int(x) for x in past],

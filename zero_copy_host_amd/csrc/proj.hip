@@ -83,6 +83,90 @@ __device__ inline void proj_store(const ProjArgs& a, const int seg, const int ns
   if (dev) *reinterpret_cast<uint4*>(reinterpret_cast<T*>(dev) + (bgk * a.T + t) * a.d + i) = val;
 }
 
+// The tile's epilogue: round to T into an LDS tile, then write whole rows (16 bytes a lane); with the
+// rotary embedding, first rotate Q and K on the fp32 accumulators (staged in LDS a band at a time).
+template <typename T, typename C>
+__device__ __attribute__((always_inline)) inline void proj_epilogue(const ProjArgs& a, f32x16 (&acc)[C::MB][C::NB],
+                                                                    unsigned char* smem, const int seg, const int nseg,
+                                                                    const int m0, const int n0, const int wm, const int wn,
+                                                                    const int lane, const int tid) {
+  constexpr int BM = C::BM, BN = C::BN, VEC = C::VEC, MB = C::MB, NB = C::NB, THREADS = C::THREADS;
+  constexpr int CH = BN / VEC;                   // 16-byte chunks per output row
+  auto store_chunk = [&](const int m, const int n, const uint4 val) __attribute__((always_inline)) {
+    proj_store<T>(a, seg, nseg, m, n, val);
+  };
+
+  if (a.rope_cs != nullptr && seg < 2) {
+    // Rotary embedding of Q and K at positions past_len[b] + t, on the fp32 accumulators before the
+    // rounding: the tile is staged in fp32, a band of wave rows at a time, and each 16-byte output
+    // chunk is formed from its own columns and their partners d/2 away in the same head (a
+    // workgroup's columns start at a multiple of 128 and hold whole heads).
+    constexpr int LDF = BN + 4;                  // padded fp32 staging row
+    constexpr int WROWS = 32 * MB;               // rows of one wave row
+    constexpr int FIT = (C::SMEM / (LDF * 4)) / WROWS;   // wave rows whose fp32 tile fits the LDS
+    constexpr int BAND = FIT >= C::WM ? C::WM : (FIT >= 2 ? 2 : 1);   // wave rows per band
+    static_assert(C::WM % BAND == 0 && BAND * WROWS * LDF * 4 <= C::SMEM, "fp32 staging band");
+    float* sF = reinterpret_cast<float*>(smem);
+    const int half = a.d / 2;
+    for (int band = 0; band < C::WM / BAND; ++band) {
+      if (wm / BAND == band) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = (wm % BAND) * WROWS + i * 32 + acc_row(v, lane);
+              sF[r * LDF + wn * 32 * NB + j * 32 + (lane & 31)] = acc[i][j][v];
+            }
+      }
+      __syncthreads();
+      for (int c = tid; c < BAND * WROWS * CH; c += THREADS) {
+        const int rl = c / CH, cc = (c % CH) * VEC;
+        const int m = m0 + band * BAND * WROWS + rl, n = n0 + cc;
+        if (m >= a.M || n >= nseg) continue;
+        const int hc = n % a.d;
+        const bool low = hc < half;
+        const int ip = low ? hc : hc - half;
+        const float* own = sF + rl * LDF + cc;
+        const float* oth = sF + rl * LDF + (low ? cc + half : cc - half);
+        const float2* cs = a.rope_cs + (size_t)m * half + ip;
+        T res[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float2 w = cs[e];
+          const float y = low ? own[e] * w.x - oth[e] * w.y : own[e] * w.x + oth[e] * w.y;
+          res[e] = Elem<T>::from_float(y);
+        }
+        uint4 val;
+        __builtin_memcpy(&val, res, 16);
+        store_chunk(m, n, val);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 32 * MB + i * 32 + acc_row(v, lane);
+        const int cc = wn * 32 * NB + j * 32 + (lane & 31);
+        sO[r * C::LDO + cc] = Elem<T>::from_float(acc[i][j][v]);
+      }
+  __syncthreads();
+  for (int c = tid; c < BM * CH; c += THREADS) {
+    const int r = c / CH, cc = (c % CH) * VEC;
+    const int m = m0 + r, n = n0 + cc;
+    if (m >= a.M || n >= nseg) continue;
+    store_chunk(m, n, *reinterpret_cast<const uint4*>(sO + r * C::LDO + cc));
+  }
+}
+
 // 16-bit types with the default tiles: one 256x256 workgroup of 8 waves per CU, two waves per
 // SIMD (256 registers a lane). Against two 128x256 workgroups per CU it loads a third fewer
 // operand bytes per MFMA into the CU.
@@ -203,80 +287,7 @@ void proj_kernel(const ProjArgs a) {
   }
   if (kt < nk) step(kt, 0, 0);
 
-  // ---- epilogue: round to T into an LDS tile, then write whole rows (16 bytes a lane)
-  constexpr int CH = BN / VEC;                   // 16-byte chunks per output row
-  auto store_chunk = [&](const int m, const int n, const uint4 val) __attribute__((always_inline)) {
-    proj_store<T>(a, seg, nseg, m, n, val);
-  };
-
-  if (a.rope_cs != nullptr && seg < 2) {
-    // Rotary embedding of Q and K at positions past_len[b] + t, on the fp32 accumulators before the
-    // rounding: the tile is staged in fp32, a band of wave rows at a time, and each 16-byte output
-    // chunk is formed from its own columns and their partners d/2 away in the same head (a
-    // workgroup's columns start at a multiple of 128 and hold whole heads).
-    constexpr int LDF = BN + 4;                  // padded fp32 staging row
-    constexpr int WROWS = 32 * MB;               // rows of one wave row
-    constexpr int BAND = (C::SMEM / (LDF * 4)) / WROWS >= C::WM ? C::WM : 2;   // wave rows per band
-    static_assert(C::WM % BAND == 0 && BAND * WROWS * LDF * 4 <= C::SMEM, "fp32 staging band");
-    float* sF = reinterpret_cast<float*>(smem);
-    const int half = a.d / 2;
-    for (int band = 0; band < C::WM / BAND; ++band) {
-      if (wm / BAND == band) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = (wm % BAND) * WROWS + i * 32 + acc_row(v, lane);
-              sF[r * LDF + wn * 32 * NB + j * 32 + (lane & 31)] = acc[i][j][v];
-            }
-      }
-      __syncthreads();
-      for (int c = tid; c < BAND * WROWS * CH; c += THREADS) {
-        const int rl = c / CH, cc = (c % CH) * VEC;
-        const int m = m0 + band * BAND * WROWS + rl, n = n0 + cc;
-        if (m >= a.M || n >= nseg) continue;
-        const int hc = n % a.d;
-        const bool low = hc < half;
-        const int ip = low ? hc : hc - half;
-        const float* own = sF + rl * LDF + cc;
-        const float* oth = sF + rl * LDF + (low ? cc + half : cc - half);
-        const float2* cs = a.rope_cs + (size_t)m * half + ip;
-        T res[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float2 w = cs[e];
-          const float y = low ? own[e] * w.x - oth[e] * w.y : own[e] * w.x + oth[e] * w.y;
-          res[e] = Elem<T>::from_float(y);
-        }
-        uint4 val;
-        __builtin_memcpy(&val, res, 16);
-        store_chunk(m, n, val);
-      }
-      __syncthreads();
-    }
-    return;
-  }
-
-  T* sO = reinterpret_cast<T*>(smem);            // [BM][LDO]
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 32 * MB + i * 32 + acc_row(v, lane);
-        const int cc = wn * 32 * NB + j * 32 + (lane & 31);
-        sO[r * C::LDO + cc] = Elem<T>::from_float(acc[i][j][v]);
-      }
-  __syncthreads();
-  for (int c = tid; c < BM * CH; c += THREADS) {
-    const int r = c / CH, cc = (c % CH) * VEC;
-    const int m = m0 + r, n = n0 + cc;
-    if (m >= a.M || n >= nseg) continue;
-    store_chunk(m, n, *reinterpret_cast<const uint4*>(sO + r * C::LDO + cc));
-  }
+  proj_epilogue<T, C>(a, acc, smem, seg, nseg, m0, n0, wm, wn, lane, tid);
 }
 
 // ---- few rows (M <= kProjSmallRows): the 256x256 tiles would leave most CUs idle (a 128-token step has
