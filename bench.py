@@ -123,7 +123,7 @@ def _oracle_threads():
     return max(1, min(16, n))
 
 
-def cpu_baseline_prefill(name, n_tokens=128):
+def cpu_baseline_prefill(name, n_tokens=384):
     """The oracle, as it is, on a bounded sample of workload `name`'s prefill step: the first
     n_tokens of the step's new tokens (every sequence, every head), on the same past keys, timed
     in the oracle's threaded C form (fp64 loops over (sequence, kv head, block of query tokens)).
