@@ -294,9 +294,10 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
 // L2 conflict-miss and are fetched again, 1.28x the host bytes against 1.02x at a quarter).
 // With more than kLongLaunchTiles query tiles per pair a launch runs many rounds of query tiles,
 // whose running-state streams pass through L2 between the uses of the super-chunk: there it
-// takes three eighths of L2 (70B-shaped prefill, 512 tiles per pair: host reads 1.15x the
-// algorithmic bytes at a half, 1.02x at three eighths, 1.00x at a quarter, for 74.2, 76.0 and
-// 80.1 ms; the 8B-shaped prefill, 128 tiles per pair, reads 1.03x at a half).
+// takes seven sixteenths of L2 (70B-shaped prefill, 512 tiles per pair, with fetcher and own-key
+// items: 3072, 3328 and 3584 keys per super-chunk read 1.014x, 1.021x and 1.028x the algorithmic
+// host bytes in 67.0, 66.1 and 66.1 ms; the 8B-shaped prefill, 128 tiles per pair, reads 1.005x
+// at a half).
 constexpr int kLongLaunchTiles = 256;
 
 int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged, int32_t q_tiles) {
@@ -309,7 +310,7 @@ int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged, int32_t q_til
   }
   const int per_xcd = std::max(1, (pairs + 7) / 8);
   const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);  // K and V
-  const size_t budget = paged ? (1u << 20) : q_tiles > kLongLaunchTiles ? (3u << 19) : (2u << 20);
+  const size_t budget = paged ? (1u << 20) : q_tiles > kLongLaunchTiles ? (7u << 18) : (2u << 20);
   size_t keys = budget / ((size_t)per_xcd * row_bytes);
   keys = std::max<size_t>(64, keys / 64 * 64);
   return (int)std::min<size_t>(keys, limit);
