@@ -357,3 +357,27 @@ def test_rope_base_validation(dkv):
     assert L.attn_prefill_rope(ctypes.byref(c), x, w, w, w, lp, 2, 16, 256, 7, out, ws, 1 << 30, 500000.0,
                                None) == -1
     assert "rope_theta" not in _err(dkv)
+
+
+def test_key_split_workspace_follows_the_pair_count(dkv):
+    """A prefill with one query tile per pair (T * G <= 256) reserves running states for its key
+    splits: 32 per pair with few pairs, fewer as pairs grow, none from 512 pairs on."""
+    L = dkv.lib()
+    r256 = lambda n: -(-n // 256) * 256
+    d, e, Hkv, Hq = 128, 2, 8, 32
+
+    def ws(B, T):
+        c = _fake_cache(dkv, B=B, Hkv=Hkv, d=d, cap=4096)
+        lens, lp = _lens([1000] * B)
+        return L.attn_workspace_bytes(0, ctypes.byref(c), B, T, Hq, lp)
+
+    def expected(B, T, splits):
+        G = Hq // Hkv
+        state = r256(B * Hkv * (-(-(T * G) // 32)) * (d // 32 * 16 + 2) * 64 * 4)
+        return (r256(B * T * Hq * d * e) + 2 * r256(B * Hkv * T * d * e) + 2 * state
+                + r256(B * T * (d // 2) * 2 * 4) + splits * state)
+
+    assert ws(1, 128) == expected(1, 128, 0)      # 512 query rows per pair: two tiles, no splits
+    assert ws(1, 16) == expected(1, 16, 32)       # 8 pairs: 32 splits each
+    assert ws(8, 16) == expected(8, 16, 8)        # 64 pairs: 8
+    assert ws(64, 16) == expected(64, 16, 0)      # 512 pairs: one split each, none reserved

@@ -266,6 +266,10 @@ bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, i
 }
 
 // ---- prefill workspace layout
+// Key splits per pair of a one-query-tile prefill at most: enough for two workgroups per CU of a
+// 256-CU device, and at most kMaxKeySplits (one split per pair from 512 pairs up: no split).
+int key_split_cap(int pairs) { return std::min(kMaxKeySplits, std::max(1, (512 + pairs - 1) / std::max(1, pairs))); }
+
 struct PrefillWs {
   size_t q, k_new, v_new, state, nstate, rope, split, total;
 };
@@ -282,9 +286,10 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   w.nstate = w.state + sb;
   w.rope = w.nstate + sb;   // rotary (cos, sin) table of the call's rows (attn_prefill_rope)
   w.split = w.rope + round_up((size_t)batch * T * (d / 2) * 2 * sizeof(float), 256);
-  // one query tile per pair: the running states of up to kMaxKeySplits key splits per pair
+  // one query tile per pair: the running states of the key splits (key_split_cap per pair)
   const bool one_tile = (long long)T * std::max(1, G) <= attn_rows_per_tile();
-  w.total = w.split + (one_tile ? kMaxKeySplits * sb : 0);
+  const int cap = key_split_cap(batch * std::max(1, c->n_kv_heads));
+  w.total = w.split + (one_tile && cap > 1 ? (size_t)cap * sb : 0);
   return w;
 }
 
@@ -491,10 +496,11 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
     for (int b = 0; b < batch; ++b) max_keys = std::max(max_keys, past_len[b] + T);
     const int kt = attn_key_tile(c->dtype, c->head_dim);
     const int tiles = (max_keys + kt - 1) / kt;
-    n_splits = std::min({kMaxKeySplits, tiles, std::max(1, (2 * cu_count() + P - 1) / P)});
+    const int cap = key_split_cap(P);   // what the workspace holds
+    n_splits = std::min({cap, tiles, std::max(1, (2 * cu_count() + P - 1) / P)});
     // a paged launch stages its keys' page ids in LDS: a split holds at most kPagedSuperchunk keys
     if (paged) n_splits = std::max(n_splits, (tiles + kPagedSuperchunk / kt - 1) / (kPagedSuperchunk / kt));
-    if (n_splits <= 1 || n_splits > kMaxKeySplits) n_splits = 0;
+    if (n_splits <= 1 || n_splits > cap) n_splits = 0;
   }
   ProjArgs pa = make_proj(c, x, wq, wk, wv, past_len, batch, T, D, n_q_heads, q, separate ? nullptr : kn,
                           separate ? nullptr : vn);

@@ -12,8 +12,8 @@ namespace dkv {
 constexpr int kMaxBatch = 256;   // sequences per call (lengths travel in kernel arguments)
 constexpr int kMaxD = 8192;      // model width held in LDS by the decode kernel
 constexpr int kPageTokens = 16;  // token rows per page of a paged host cache
-constexpr int kProjSmallRows = 256;
-constexpr int kMaxKeySplits = 32;     // key splits per pair at most, prefills of one query tile per pair   // projections of at most this many token rows take the small-tile kernel
+constexpr int kProjSmallRows = 256;   // projections of at most this many token rows take the small-tile kernel
+constexpr int kMaxKeySplits = 32;     // key splits per pair at most, prefills of one query tile per pair
 constexpr int kPagedDecodeChunk = 8192;  // keys per decode split at most, paged caches
 constexpr int kPagedSuperchunk = 16384;  // keys per prefill launch at most, paged caches
 constexpr int kWave = 64;
