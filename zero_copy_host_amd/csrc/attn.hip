@@ -44,6 +44,9 @@ namespace dkv {
 #ifndef DKV_ATTN_MINWAVES
 #define DKV_ATTN_MINWAVES 2   // waves per SIMD the register allocation must allow (d = 128)
 #endif
+#ifndef DKV_ATTN_KPREF
+#define DKV_ATTN_KPREF 4   // K fragments read from LDS ahead of the score products
+#endif
 #ifndef DKV_ATTN_KPAD
 #define DKV_ATTN_KPAD 8    // elements of padding per K tile row (16-bit types)
 #endif
@@ -276,15 +279,26 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
     // ---- the three parts of a key tile (KT keys) against this wave's 32 query rows
     typedef f32x16 Scores[KT / 32];                      // Sᵀ: KT/32 blocks of 32 keys x 32 queries
     typedef typename MF::frag Probs[KT / 32][32 / KSTEP];  // Pᵀ in MFMA operand form
+    // The K fragments are read from LDS PD products ahead of their use, and the KT/32 key blocks'
+    // product chains are interleaved (fragment f is key block f % NKB, reduction step f / NKB):
+    // left to itself the compiler reads each fragment into the same registers right before its
+    // product and waits for it, so every product paid the full LDS latency. Each chain still sums
+    // its steps in ascending order, so the scores are unchanged bit for bit.
     auto qk = [&](const T* tK, Scores& sc) __attribute__((always_inline)) {
+      constexpr int NKB = KT / 32, NF = NKB * (DH / KSTEP), PD = DKV_ATTN_KPREF < NF ? DKV_ATTN_KPREF : NF;
+      auto kfrag = [&](const int f) __attribute__((always_inline)) {
+        return *reinterpret_cast<const typename MF::frag*>(tK + ((f % NKB) * 32 + col) * LDK + (f / NKB) * KSTEP +
+                                                           half * KPL);
+      };
+      typename MF::frag kf[PD];
 #pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb) {
+      for (int f = 0; f < PD; ++f) kf[f] = kfrag(f);
 #pragma unroll
-        for (int ks = 0; ks < DH / KSTEP; ++ks) {
-          const typename MF::frag ka =
-              *reinterpret_cast<const typename MF::frag*>(tK + (kb * 32 + col) * LDK + ks * KSTEP + half * KPL);
-          sc[kb] = MF::mma(ka, qf[ks], ks == 0 ? f32x16{} : sc[kb]);
-        }
+      for (int f = 0; f < NF; ++f) {
+        const int kb = f % NKB, ks = f / NKB;
+        sc[kb] = MF::mma(kf[f % PD], qf[ks], ks == 0 ? f32x16{} : sc[kb]);
+        if (f + PD < NF) kf[f % PD] = kfrag(f + PD);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // mask, tile maximum and the lazy raise of the reference maximum (rescaling o and l);
