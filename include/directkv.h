@@ -51,6 +51,19 @@ extern "C" {
  *   DIRECTKV_PREFILL_CHUNK=<keys>  keys per prefill super-chunk (rounded down to a multiple of
  *                                  64), instead of the L2-sized default; rounding order of the
  *                                  attention changes, not the result within tolerance;
+ *   DIRECTKV_PREFILL_CHUNKED=0     prefills with several super-chunks and query tiles take one
+ *                                  launch per super-chunk instead of the two-launch form (a
+ *                                  chunk launch of every super-chunk's items, then a finish
+ *                                  launch); rounding order changes, not the result within
+ *                                  tolerance;
+ *   DIRECTKV_PREFILL_INSERT=<n>    two-launch form: items of a super-chunk dispatched before
+ *                                  the next one's fetchers (dispatch order only: bitwise the
+ *                                  same output);
+ *   DIRECTKV_PREFILL_OWN=<percent> two-launch form: share of the own-key work in the chunk
+ *                                  launch; rounding order changes, not the result within
+ *                                  tolerance;
+ *   DIRECTKV_PREFILL_FETCHERS=<n>  past-key items per pair dispatched first in a launch
+ *                                  (dispatch order only: bitwise the same output);
  *   DIRECTKV_DECODE_QPASS=0|1      decode q projected inside the attention kernel (0) or by the
  *                                  pre-pass (1); bitwise the same queries;
  *   DIRECTKV_DECODE_COMBINE=1      keep the combine launch when every sequence has one split;

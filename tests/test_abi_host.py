@@ -149,9 +149,13 @@ def test_workspace_sizes(dkv):
     # queries + new K + new V + two fp32 running states (past keys, this step's own keys): per 32
     # query rows, 64 lanes x (d/32 * 16 accumulators + m + l); then the rotary (cos, sin) fp32 table
     # of every new row's d/2 pairs
-    want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 2 * 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
+    state = 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
+    want = 8192 * 32 * 128 * e + 2 * 8 * 8192 * 128 * e + 2 * state
     want += 8192 * 64 * 2 * 4
-    assert want <= ws <= want + 6 * 256
+    # the two-launch prefill: one more state per past super-chunk of 3072 keys (8 pairs, one per
+    # XCD, 1.5 MiB of K and V each) for any past length up to capacity - T = 24576: 8 of them
+    want += 8 * state
+    assert want <= ws <= want + 7 * 256
     wsd = L.attn_workspace_bytes(1, ctypes.byref(c), 1, 1, 32, lp)
     # decode: fp32 partials (o, m, l) for at most 2 * (2 * 256 / Hkv) + B + 1 splits (the split
     # target doubles for short chunks), then the fp32 queries [B][Hq*d] the pre-pass projects
@@ -164,6 +168,36 @@ def test_workspace_sizes(dkv):
     assert L.attn_workspace_bytes(3, ctypes.byref(c), 1, 1, 32, lp) == staging + wsd
     assert L.attn_workspace_bytes(4, ctypes.byref(c), 1, 1, 32, lp) == 0
     assert L.attn_workspace_bytes(1, None, 1, 1, 32, lp) == 0
+
+
+def test_workspace_two_launch_prefill_region(dkv):
+    """The super-chunk states of the two-launch prefill: present only where they fit 2 GiB and the
+    call has more than one query tile per pair and more than one super-chunk of past keys."""
+    L = dkv.lib()
+    lens, lp = _lens([0, 0])
+
+    def up(n):
+        return (n + 255) // 256 * 256
+
+    def ws(B, Hkv, cap, T, Hq):
+        c = _fake_cache(dkv, B=B, Hkv=Hkv, d=128, cap=cap)
+        return L.attn_workspace_bytes(0, ctypes.byref(c), B, T, Hq, lp)
+
+    def state(B, Hkv, T, G):
+        return up(B * Hkv * (T * G // 32) * (4 * 16 + 2) * 64 * 4)
+
+    def base(B, Hkv, T, Hq):   # queries, new K and V, two running states, rotary table (bf16, d = 128)
+        G = Hq // Hkv
+        return (up(B * T * Hq * 128 * 2) + 2 * up(B * Hkv * T * 128 * 2) + 2 * state(B, Hkv, T, G)
+                + up(B * T * 64 * 2 * 4))
+
+    # 70B-shaped (B=2, Hkv=8, G=8, T=16384, capacity 65600): 17 super-chunks x 1.09 GB is over the
+    # cap, so the launch-per-super-chunk path runs and there is no region
+    assert ws(2, 8, 65600, 16384, 64) == base(2, 8, 16384, 64)
+    # at most one super-chunk of 3072 past keys: no region
+    assert ws(1, 8, 8192 + 3072, 8192, 32) == base(1, 8, 8192, 32)
+    # two super-chunks: two states
+    assert ws(1, 8, 8192 + 3073, 8192, 32) == base(1, 8, 8192, 32) + 2 * state(1, 8, 8192, 4)
 
 
 # ---- paged cache: the block table is checked on the host before anything is enqueued
@@ -377,7 +411,9 @@ def test_key_split_workspace_follows_the_pair_count(dkv):
         return (r256(B * T * Hq * d * e) + 2 * r256(B * Hkv * T * d * e) + 2 * state
                 + r256(B * T * (d // 2) * 2 * 4) + splits * state)
 
-    assert ws(1, 128) == expected(1, 128, 0)      # 512 query rows per pair: two tiles, no splits
+    # 512 query rows per pair: two tiles, no key splits; the two-launch prefill's states instead, one
+    # per super-chunk of 3072 keys for past lengths up to 4096 - 128
+    assert ws(1, 128) == expected(1, 128, 2)
     assert ws(1, 16) == expected(1, 16, 32)       # 8 pairs: 32 splits each
     assert ws(8, 16) == expected(8, 16, 8)        # 64 pairs: 8
     assert ws(64, 16) == expected(64, 16, 0)      # 512 pairs: one split each, none reserved

@@ -48,9 +48,13 @@ def _ids(s):
     return f"B{s[0]}-T{s[1]}-L{max(s[2])}-G{s[4] // s[5]}-d{s[6]}-{s[7]}-sk{s[8]}"
 
 
+@pytest.mark.parametrize("two_launch", ["1", "0"], ids=["two-launch", "per-chunk"])
 @pytest.mark.parametrize("shape", PREFILL, ids=_ids)
-def test_prefill_large_growing_scores(shape, monkeypatch):
+def test_prefill_large_growing_scores(shape, two_launch, monkeypatch):
+    """Both multi-super-chunk paths: the two-launch prefill (each super-chunk's state kept apart,
+    merged at the end) and the launch-per-super-chunk path (one running state carried along)."""
     B, T, past, D, Hq, Hkv, d, dtype, sk = shape
+    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNKED", two_launch)
     if sk is not None:
         monkeypatch.setenv("DIRECTKV_PREFILL_CHUNK", str(sk))
     case = _case(31, B, T, past, D, Hq, Hkv, d, dtype)

@@ -158,7 +158,10 @@ def test_paged_decode_equals_contiguous_bitwise(dtype, d, G):
 @pytest.mark.parametrize("chunk", [None, "64"])
 def test_paged_prefill_equals_contiguous_bitwise(chunk, monkeypatch):
     """Several super-chunks (chunk 64: many launches, the new rows stored by several of
-    them), ragged query tiles, two sequences of different lengths."""
+    them), ragged query tiles, two sequences of different lengths. A paged cache always takes the
+    launch-per-super-chunk path, so the contiguous run is held to that path too (the two-launch
+    prefill merges the super-chunks' states in another order)."""
+    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNKED", "0")
     if chunk:
         monkeypatch.setenv("DIRECTKV_PREFILL_CHUNK", chunk)
     case = _case(302, 2, 70, [33, 130], 256, 8, 2, 128, "bf16")

@@ -271,10 +271,13 @@ bool decode_uses_qpass(const dkv_cache* c, const DecodePlan& p, int32_t batch, i
 int key_split_cap(int pairs) { return std::min(kMaxKeySplits, std::max(1, (512 + pairs - 1) / std::max(1, pairs))); }
 
 struct PrefillWs {
-  size_t q, k_new, v_new, state, nstate, rope, split, total;
+  size_t q, k_new, v_new, state, nstate, rope, split, chunk, total;
+  int n_chunks;   // past super-chunk states the two-launch prefill has room for (0: not used)
 };
 
-PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads) {
+int chunked_max(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads, bool paged);
+
+PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads, bool paged = false) {
   PrefillWs w;
   const size_t e = elem_size(c->dtype), d = c->head_dim;
   const int G = n_q_heads / std::max(1, c->n_kv_heads);
@@ -289,7 +292,10 @@ PrefillWs prefill_layout(const dkv_cache* c, int32_t batch, int32_t T, int32_t n
   // one query tile per pair: the running states of the key splits (key_split_cap per pair)
   const bool one_tile = (long long)T * std::max(1, G) <= attn_rows_per_tile();
   const int cap = key_split_cap(batch * std::max(1, c->n_kv_heads));
-  w.total = w.split + (one_tile && cap > 1 ? (size_t)cap * sb : 0);
+  w.chunk = w.split + (one_tile && cap > 1 ? (size_t)cap * sb : 0);
+  // the two-launch prefill: one running state per past super-chunk
+  w.n_chunks = chunked_max(c, batch, T, n_q_heads, paged);
+  w.total = w.chunk + (size_t)w.n_chunks * sb;
   return w;
 }
 
@@ -332,6 +338,71 @@ int prefill_fetchers() {
     if (v >= 0 && v <= 64) return (int)v;
   }
   return 8;
+}
+
+// The two-launch prefill (attn_kernel, chunked mode): one launch runs the past-key items of every
+// super-chunk, each leaving its own state, with the next super-chunk's fetchers dispatched while the
+// current one's items compute, so the link works beside the MFMA pipes instead of ahead of them;
+// a second launch runs the heavier own-key items, which fold every state in as they finalise.
+// Two super-chunks then share an XCD's L2, three eighths of it each. It is used where every
+// super-chunk's state fits kChunkStateCap of workspace (not for a paged cache), else the
+// launch-per-super-chunk path runs (DIRECTKV_PREFILL_CHUNKED=0 forces that path).
+constexpr size_t kChunkStateCap = (size_t)2 << 30;
+
+int chunk_group(int P) { return P % 8 == 0 ? 8 : P; }
+
+int chunked_keys(const dkv_cache* c, int32_t group) {
+  if (const char* env = getenv("DIRECTKV_PREFILL_CHUNK")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 64) return (int)(v / 64 * 64);
+  }
+  const int per_xcd = std::max(1, (group + 7) / 8);
+  const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);
+  const size_t keys = (size_t)(3u << 19) / ((size_t)per_xcd * row_bytes);
+  return (int)std::max<size_t>(64, keys / 64 * 64);
+}
+
+bool chunked_enabled() {
+  const char* env = getenv("DIRECTKV_PREFILL_CHUNKED");
+  return !(env && env[0] == '0');
+}
+
+// super-chunk states the workspace holds for the two-launch prefill: enough for any past length
+// up to capacity - T, or 0 where the mode is not used
+int chunked_max(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads, bool paged) {
+  if (paged || c->n_kv_heads <= 0) return 0;
+  const int G = std::max(1, n_q_heads / c->n_kv_heads);
+  if ((long long)T * G <= attn_rows_per_tile()) return 0;   // one query tile per pair: key splits
+  const long long max_past = (long long)c->capacity - T;
+  const int ck = chunked_keys(c, chunk_group(batch * c->n_kv_heads));
+  const long long S = (max_past + ck - 1) / ck;
+  const size_t sb = round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, G), 256);
+  if (S < 2 || (size_t)S * sb > kChunkStateCap) return 0;
+  return (int)S;
+}
+
+// own-key items of the two-launch prefill's first launch: the lightest query tiles, about a third
+// of the own-key work (DIRECTKV_PREFILL_OWN=<percent> overrides it for tuning)
+int chunked_own_percent() {
+  if (const char* env = getenv("DIRECTKV_PREFILL_OWN")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 0 && v <= 100) return (int)v;
+  }
+  return 33;
+}
+
+// chunk j's items per pair dispatched ahead of chunk j+1's fetchers: five sixths of them, so the
+// next super-chunk crosses the link during the last sixth of this one's items and the fetchers'
+// own compute. Earlier, the two super-chunks and the running-state streams overflow L2: 8B-shaped
+// prefill (120 such items per pair) with 40, 100 and 120 read 1.153x, 1.014x and about 1.01x the
+// algorithmic host bytes, in 4.62-4.72 ms for all from 60 on (DIRECTKV_PREFILL_INSERT=<items>
+// overrides it for tuning).
+int chunked_insert(int items) {
+  if (const char* env = getenv("DIRECTKV_PREFILL_INSERT")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 0) return (int)std::min<long>(v, items);
+  }
+  return items * 5 / 6;
 }
 
 // block table of a paged cache, already copied into device memory (null: contiguous cache)
@@ -467,7 +538,7 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
                 const void* wv, const int32_t* past_len, int32_t batch, int32_t T, int32_t D, int32_t n_q_heads,
                 void* out, void* ws, size_t ws_bytes, hipStream_t s, int32_t variant, double rope = 0.0) {
   const bool paged = pg.table != nullptr;
-  const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads);
+  const PrefillWs lay = prefill_layout(c, batch, T, n_q_heads, paged);
   if (!ws || ws_bytes < lay.total || !aligned16(ws))
     return fail(DKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu (16-byte aligned)", ws_bytes, lay.total);
   const int G = n_q_heads / c->n_kv_heads;
@@ -623,6 +694,44 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
     for (int k0 = 0; k0 < max_past; k0 += skp) ranges.emplace_back(k0, std::min(k0 + skp, max_past));
     const int S = (int)ranges.size();
     aa.clip_past = 1;
+    // own-key work of query tile q: the rows' visible own keys, sum over rows of (row / G + 1)
+    std::vector<double> cum(Q + 1, 0.0);
+    for (int qt = 0; qt < Q; ++qt) {
+      const long long r0 = (long long)qt * rows, r1 = std::min<long long>((long long)T * G, r0 + rows) - 1;
+      double wq = 0.0;
+      for (long long t = r0 / G; t <= r1 / G; ++t)
+        wq += (double)(std::min<long long>(r1, (t + 1) * G - 1) - std::max<long long>(r0, t * G) + 1) * (double)(t + 1);
+      cum[qt + 1] = cum[qt] + wq;
+    }
+    {
+      // the two-launch prefill, where its super-chunks' states fit the workspace
+      const int ck = chunked_keys(c, group);
+      const int nc = max_past > 0 ? (max_past + ck - 1) / ck : 0;
+      const int ckp = nc > 0 ? std::min<int>(ck, (int)round_up((max_past + nc - 1) / nc, 64)) : ck;
+      const int SC = nc > 0 ? (max_past + ckp - 1) / ckp : 0;
+      if (!paged && SC >= 2 && SC <= lay.n_chunks && chunked_enabled()) {
+        int qa = 0;
+        const double goal = cum[Q] * chunked_own_percent() / 100.0;
+        while (qa < Q && cum[qa + 1] <= goal + 1e-9) ++qa;
+        const int F = std::min(aa.fetchers, Q);
+        aa.chunked = 1;
+        aa.n_splits = SC;
+        aa.split_stride = (int64_t)(round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, G), 256) /
+                                    sizeof(float));
+        aa.chunk_keys = ckp;
+        aa.chunk_insert = chunked_insert(Q - F);
+        aa.n_own0 = qa;
+        aa.state = reinterpret_cast<float*>(w + lay.chunk);
+        int st = launch();
+        if (st) return st;
+        aa.chunked = 2;
+        if ((st = launch())) return st;
+        aa.chunked = 0;
+        aa.n_splits = 0;
+        aa.state = state;
+        continue;
+      }
+    }
     if (S <= 1) {
       aa.past_items = 0;
       aa.dev_q0 = 0;
@@ -643,15 +752,6 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
       aa.first = aa.last = aa.merge_new = 1;
       if ((st = launch())) return st;
       continue;
-    }
-    // own-key work of query tile q: the rows' visible own keys, sum over rows of (row / G + 1)
-    std::vector<double> cum(Q + 1, 0.0);
-    for (int qt = 0; qt < Q; ++qt) {
-      const long long r0 = (long long)qt * rows, r1 = std::min<long long>((long long)T * G, r0 + rows) - 1;
-      double wq = 0.0;
-      for (long long t = r0 / G; t <= r1 / G; ++t)
-        wq += (double)(std::min<long long>(r1, (t + 1) * G - 1) - std::max<long long>(r0, t * G) + 1) * (double)(t + 1);
-      cum[qt + 1] = cum[qt] + wq;
     }
     int dq = 0;
     for (int i = 0; i < S; ++i) {
@@ -1142,7 +1242,7 @@ size_t attn_paged_workspace_bytes(int32_t phase, const dkv_paged_cache* c, int32
   if (phase == 2) return tb;
   if (n_q_heads <= 0) return 0;
   if (phase == 1) return tb + decode_ws_bytes(&view, batch, n_q_heads, true);
-  if (phase == 0) return tb + prefill_layout(&view, batch, T, n_q_heads).total;
+  if (phase == 0) return tb + prefill_layout(&view, batch, T, n_q_heads, true).total;
   return 0;
 }
 
@@ -1207,7 +1307,7 @@ int attn_prefill_paged(const dkv_paged_cache* c, const int32_t* block_table, int
     return fail(DKV_ERR_INVALID_ARG, "batch must be in [1, %d], max_pages positive and T >= 0", kMaxBatch);
   if (n_q_heads <= 0) return fail(DKV_ERR_INVALID_ARG, "n_q_heads must be positive");
   const dkv_cache pre = paged_view(c, batch, max_pages);
-  const size_t need = prefill_layout(&pre, batch, T, n_q_heads).total;
+  const size_t need = prefill_layout(&pre, batch, T, n_q_heads, true).total;
   st = paged_front(c, block_table, max_pages, past_len, batch, T, ws, ws_bytes, need, view, rest, rest_bytes);
   if (st) return st;
   if ((st = check_call(&view, batch, T, D, past_len, {x, wq, wk, wv, out}))) return st;

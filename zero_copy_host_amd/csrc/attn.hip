@@ -89,6 +89,7 @@ constexpr float kLazyRescale = 8.f;   // log2 units: raise the reference max pas
 struct AttnItem {
   int p, qt, kc0, kc1, first, last, merge;
   float* state;
+  int split0 = 1;   // finalising with key splits: the first split state folded in (0: all of them)
 };
 
 // A 16-byte load of a key or value row piece; NT: non-temporal (the line is the first L2 evicts),
@@ -492,11 +493,11 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
 
   if (it.last) {
     if (a.n_splits && wvalid) {
-      // key-split mode: fold in the states of splits 1 .. n_splits - 1 (this item read split 0's).
-      // A split whose keys this row cannot see left m = -inf and is skipped; split 0 starts at key
-      // 0, which every row sees, unless it is empty (fewer key tiles than splits): then the first
-      // split with keys is taken as it is.
-      for (int j = 1; j < a.n_splits; ++j) {
+      // key-split mode: fold in the states of splits split0 .. n_splits - 1 (an item with split0 = 1
+      // read split 0's as its running state). A split whose keys this row cannot see left m = -inf
+      // and is skipped; if the running state is still empty (split 0 without keys, or no keys
+      // computed yet), the first split with keys is taken as it is.
+      for (int j = it.split0; j < a.n_splits; ++j) {
         const float* ns = it.state + (size_t)j * a.split_stride + st_off;
         const float m2 = __builtin_nontemporal_load(ns + DB * 16 * 64 + lane);
         if (m2 == -INFINITY) continue;
@@ -574,10 +575,83 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
 // and leaves its running state in that split's state array; a.split_storers more workgroups
 // write this step's new rows to the host cache meanwhile (the storer role). A second launch
 // (a.split_combine) folds the splits' states together per pair and writes the output.
+// This workgroup's pair and its position in that pair's sequence of items: with XCD placement
+// pair p is served by XCD p % 8 (workgroup i runs on XCD i % 8); false for a padding workgroup.
+__device__ inline bool attn_pair_slot(const AttnArgs& a, int& p, int& r) {
+  const int P = a.pairs;
+  if (a.xcd_group) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int ppx = (P + 7) >> 3;
+    const int lp = (slot % ppx) * 8 + xcd;
+    if (lp >= P) return false;
+    p = a.pair0 + lp;
+    r = slot / ppx;
+  } else {
+    p = a.pair0 + blockIdx.x % P;
+    r = blockIdx.x / P;
+  }
+  return true;
+}
+
 template <typename T, int DH, int G, bool PAGED>
 __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWAVES)
 void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds<T, DH, PAGED> lds;
+  if (a.chunked) {
+    // Two-launch prefill over past super-chunks. Per pair the chunk launch runs, in dispatch
+    // order: F fetcher items of chunk 0, the own-key items of query tiles [0, n_own0), then per
+    // chunk j its other items with chunk j+1's F fetchers inserted after the first chunk_insert of
+    // them, so chunk j+1 crosses the link while chunk j's items compute from L2. Every past item
+    // starts fresh and leaves its state in chunk j's array; no item waits for another. The finish
+    // launch runs the own-key items of [n_own0, Q), which fold in every chunk's state as they
+    // finalise, and for [0, n_own0) items that only merge the chunk states and the own-key state.
+    int p, r;
+    if (!attn_pair_slot(a, p, r)) return;
+    const int Q = a.q_tiles, S = a.n_splits, F = min(a.fetchers, Q), Qa = a.n_own0;
+    const int L = a.past_len[p / a.Hkv];
+    constexpr int TPT = AttnCfg<T, DH>::ROWS / G;   // tokens per query tile
+    if (a.chunked == 2) {
+      if (r < Q - Qa) {
+        const int qt = Q - 1 - r;
+        if (a.store_new) attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
+        AttnItem it{p, qt, L, L + a.T, 1, 1, 0, a.state};
+        it.split0 = 0;
+        attn_item<T, DH, G, PAGED, false>(a, it, lds);
+      } else {
+        attn_item<T, DH, G, PAGED>(a, AttnItem{p, Q - 1 - r, 0, 0, 0, 1, 1, a.state}, lds);
+      }
+      return;
+    }
+    if (r >= F && r < F + Qa) {
+      const int qt = Qa - 1 - (r - F);
+      if (a.store_new) attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
+      attn_item<T, DH, G, PAGED, true>(a, AttnItem{p, qt, L, L + a.T, 1, 0, 0, a.nstate}, lds);
+      return;
+    }
+    int j, idx;
+    if (r < F) {
+      j = 0;
+      idx = r;
+    } else {
+      const int ins = min(a.chunk_insert, Q - F);
+      const int o0 = r - F - Qa;
+      j = min(o0 / Q, S - 1);                    // block j: Q - F of chunk j's items + F of chunk j+1's
+      const int o = o0 - j * Q;
+      const int fj = j + 1 < S ? F : 0;
+      if (o < ins) {
+        idx = F + o;
+      } else if (o < ins + fj) {
+        idx = o - ins;
+        j += 1;
+      } else {
+        idx = F + o - fj;
+      }
+    }
+    const int kc0 = min(j * a.chunk_keys, L), kc1 = min(kc0 + a.chunk_keys, L);
+    attn_item<T, DH, G, PAGED>(a, AttnItem{p, Q - 1 - idx, kc0, kc1, 1, 0, 0, a.state + (size_t)j * a.split_stride},
+                               lds);
+    return;
+  }
   if (a.n_splits) {
     if (!a.split_combine && (int)blockIdx.x >= a.pairs * a.n_splits) {
       // storer workgroup s: an equal share of the (pair, token) rows of this step, K and V, from
@@ -608,19 +682,8 @@ void attn_kernel(const AttnArgs a) {
     }
     return;
   }
-  const int P = a.pairs;
   int p, r;   // pair, and the item's position in that pair's sequence of items
-  if (a.xcd_group) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int ppx = (P + 7) >> 3;
-    const int lp = (slot % ppx) * 8 + xcd;
-    if (lp >= P) return;
-    p = a.pair0 + lp;
-    r = slot / ppx;
-  } else {
-    p = a.pair0 + blockIdx.x % P;
-    r = blockIdx.x / P;
-  }
+  if (!attn_pair_slot(a, p, r)) return;
   const int Q = a.q_tiles;
   const int F = a.past_items ? min(a.fetchers, Q) : 0;
   const int ND = a.dev_q1 - a.dev_q0;
@@ -647,10 +710,13 @@ void attn_kernel(const AttnArgs a) {
 template <typename T, int DH, int G, bool PAGED>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int P = a.pairs;
-  const int items = a.n_splits ? (a.split_combine ? 1 : a.n_splits)
-                               : (a.past_items ? a.q_tiles : 0) + a.dev_q1 - a.dev_q0;   // per pair
-  const int grid = a.xcd_group && !a.n_splits ? 8 * ((P + 7) / 8) * items
-                                              : P * items + (a.n_splits && !a.split_combine ? a.split_storers : 0);
+  const int items = a.chunked == 1 ? a.n_splits * a.q_tiles + a.n_own0
+                    : a.chunked == 2 ? a.q_tiles
+                    : a.n_splits   ? (a.split_combine ? 1 : a.n_splits)
+                                   : (a.past_items ? a.q_tiles : 0) + a.dev_q1 - a.dev_q0;   // per pair
+  const bool placed = a.xcd_group && (a.chunked || !a.n_splits);
+  const int grid = placed ? 8 * ((P + 7) / 8) * items
+                          : P * items + (a.n_splits && !a.chunked && !a.split_combine ? a.split_storers : 0);
   hipLaunchKernelGGL((attn_kernel<T, DH, G, PAGED>), dim3(grid), dim3(AttnCfg<T, DH>::THREADS), 0, s, a);
   return hipGetLastError();
 }

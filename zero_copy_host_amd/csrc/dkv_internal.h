@@ -231,6 +231,11 @@ struct AttnArgs {
   int64_t split_stride;     // key-split mode: floats between two splits' state arrays (from `state`)
   int32_t split_storers;    // key-split mode: workgroups after the split items that copy this step's
                             // new K/V rows from their device copies to the host cache
+  int32_t chunked;          // two-launch prefill: 1 = the chunk launch, 2 = the finish launch, 0 = off
+                            // (n_splits = past super-chunks, split_stride = floats between their states)
+  int32_t chunk_keys;       // two-launch prefill: keys per past super-chunk
+  int32_t chunk_insert;     // two-launch prefill: chunk j's items dispatched before chunk j+1's fetchers
+  int32_t n_own0;           // two-launch prefill: own-key items of query tiles [0, n_own0) in the chunk launch
   const int32_t* table;     // paged cache: device block table [B][max_pages] (paged instances)
   int32_t max_pages;
   int32_t past_len[kMaxBatch];
