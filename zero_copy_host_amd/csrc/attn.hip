@@ -597,6 +597,12 @@ template <typename T, int DH, int G, bool PAGED>
 __global__ __launch_bounds__(64 * DKV_ATTN_WAVES, DKV_ATTN_MINWAVES)
 void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds<T, DH, PAGED> lds;
+  // Each mode below only picks this workgroup's item; one call at the end runs it, so the item's
+  // code is compiled twice (with and without non-temporal K/V loads), not once per kind of item.
+  AttnItem it;
+  bool nt = false;      // non-temporal K/V loads: own-key items sharing a launch with past-key items
+  int s0 = 0, s1 = 0;   // the storer role: tokens [s0, s1) of pair it.p whose new rows go to the host
+  constexpr int TPT = AttnCfg<T, DH>::ROWS / G;   // tokens per query tile
   if (a.chunked) {
     // Two-launch prefill over past super-chunks. Per pair the chunk launch runs, in dispatch
     // order: F fetcher items of chunk 0, the own-key items of query tiles [0, n_own0), then per
@@ -609,50 +615,44 @@ void attn_kernel(const AttnArgs a) {
     if (!attn_pair_slot(a, p, r)) return;
     const int Q = a.q_tiles, S = a.n_splits, F = min(a.fetchers, Q), Qa = a.n_own0;
     const int L = a.past_len[p / a.Hkv];
-    constexpr int TPT = AttnCfg<T, DH>::ROWS / G;   // tokens per query tile
     if (a.chunked == 2) {
+      const int qt = Q - 1 - r;
       if (r < Q - Qa) {
-        const int qt = Q - 1 - r;
-        if (a.store_new) attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
-        AttnItem it{p, qt, L, L + a.T, 1, 1, 0, a.state};
+        it = AttnItem{p, qt, L, L + a.T, 1, 1, 0, a.state};
         it.split0 = 0;
-        attn_item<T, DH, G, PAGED, false>(a, it, lds);
+        if (a.store_new) s0 = qt * TPT, s1 = min((qt + 1) * TPT, a.T);
       } else {
-        attn_item<T, DH, G, PAGED>(a, AttnItem{p, Q - 1 - r, 0, 0, 0, 1, 1, a.state}, lds);
+        it = AttnItem{p, qt, 0, 0, 0, 1, 1, a.state};
       }
-      return;
-    }
-    if (r >= F && r < F + Qa) {
+    } else if (r >= F && r < F + Qa) {
       const int qt = Qa - 1 - (r - F);
-      if (a.store_new) attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
-      attn_item<T, DH, G, PAGED, true>(a, AttnItem{p, qt, L, L + a.T, 1, 0, 0, a.nstate}, lds);
-      return;
-    }
-    int j, idx;
-    if (r < F) {
-      j = 0;
-      idx = r;
+      it = AttnItem{p, qt, L, L + a.T, 1, 0, 0, a.nstate};
+      nt = true;
+      if (a.store_new) s0 = qt * TPT, s1 = min((qt + 1) * TPT, a.T);
     } else {
-      const int ins = min(a.chunk_insert, Q - F);
-      const int o0 = r - F - Qa;
-      j = min(o0 / Q, S - 1);                    // block j: Q - F of chunk j's items + F of chunk j+1's
-      const int o = o0 - j * Q;
-      const int fj = j + 1 < S ? F : 0;
-      if (o < ins) {
-        idx = F + o;
-      } else if (o < ins + fj) {
-        idx = o - ins;
-        j += 1;
+      int j, idx;
+      if (r < F) {
+        j = 0;
+        idx = r;
       } else {
-        idx = F + o - fj;
+        const int ins = min(a.chunk_insert, Q - F);
+        const int o0 = r - F - Qa;
+        j = min(o0 / Q, S - 1);                    // block j: Q - F of chunk j's items + F of chunk j+1's
+        const int o = o0 - j * Q;
+        const int fj = j + 1 < S ? F : 0;
+        if (o < ins) {
+          idx = F + o;
+        } else if (o < ins + fj) {
+          idx = o - ins;
+          j += 1;
+        } else {
+          idx = F + o - fj;
+        }
       }
+      const int kc0 = min(j * a.chunk_keys, L), kc1 = min(kc0 + a.chunk_keys, L);
+      it = AttnItem{p, Q - 1 - idx, kc0, kc1, 1, 0, 0, a.state + (size_t)j * a.split_stride};
     }
-    const int kc0 = min(j * a.chunk_keys, L), kc1 = min(kc0 + a.chunk_keys, L);
-    attn_item<T, DH, G, PAGED>(a, AttnItem{p, Q - 1 - idx, kc0, kc1, 1, 0, 0, a.state + (size_t)j * a.split_stride},
-                               lds);
-    return;
-  }
-  if (a.n_splits) {
+  } else if (a.n_splits) {
     if (!a.split_combine && (int)blockIdx.x >= a.pairs * a.n_splits) {
       // storer workgroup s: an equal share of the (pair, token) rows of this step, K and V, from
       // the device copies to the host cache, while the split items compute
@@ -670,41 +670,39 @@ void attn_kernel(const AttnArgs a) {
     }
     const int p = a.pair0 + (int)blockIdx.x % a.pairs;
     if (a.split_combine) {
-      attn_item<T, DH, G, PAGED>(a, AttnItem{p, 0, 0, 0, 0, 1, 0, a.state}, lds);
+      it = AttnItem{p, 0, 0, 0, 0, 1, 0, a.state};
     } else {
       constexpr int KT = AttnCfg<T, DH>::KT;
       const int j = (int)blockIdx.x / a.pairs;
       const int nk = a.past_len[p / a.Hkv] + a.T;                 // the pair's keys, past and own
       const int tiles = (nk + KT - 1) / KT;
       const int t0 = (int)((long long)tiles * j / a.n_splits), t1 = (int)((long long)tiles * (j + 1) / a.n_splits);
-      attn_item<T, DH, G, PAGED>(a, AttnItem{p, 0, t0 * KT, min(t1 * KT, nk), 1, 0, 0, a.state + (size_t)j * a.split_stride},
-                                 lds);
+      it = AttnItem{p, 0, t0 * KT, min(t1 * KT, nk), 1, 0, 0, a.state + (size_t)j * a.split_stride};
     }
-    return;
-  }
-  int p, r;   // pair, and the item's position in that pair's sequence of items
-  if (!attn_pair_slot(a, p, r)) return;
-  const int Q = a.q_tiles;
-  const int F = a.past_items ? min(a.fetchers, Q) : 0;
-  const int ND = a.dev_q1 - a.dev_q0;
-  const int L = a.past_len[p / a.Hkv];
-  // query tiles go out last row first: under the causal mask later rows see more keys
-  if (r >= F && r < F + ND) {
-    const int qt = a.dev_q1 - 1 - (r - F);
-    // the storer role: this item's query tile's tokens' new K/V rows go to the host cache (each
-    // query tile has exactly one own-key item, so every new row is written once)
-    if (a.store_new) {
-      constexpr int TPT = AttnCfg<T, DH>::ROWS / G;   // tokens per query tile
-      attn_store<T, DH, PAGED>(a, p, qt * TPT, min((qt + 1) * TPT, a.T));
-    }
-    const AttnItem it{p, qt, L, L + a.T, 1, a.dev_final, 0, a.nstate};
-    if (a.past_items) attn_item<T, DH, G, PAGED, true>(a, it, lds);
-    else attn_item<T, DH, G, PAGED, false>(a, it, lds);
   } else {
-    const int qt = Q - 1 - (r < F ? r : r - ND);
-    const int kc1 = a.clip_past ? min(a.kc1, L) : a.kc1;
-    attn_item<T, DH, G, PAGED>(a, AttnItem{p, qt, a.kc0, kc1, a.first, a.last, a.merge_new, a.state}, lds);
+    int p, r;   // pair, and the item's position in that pair's sequence of items
+    if (!attn_pair_slot(a, p, r)) return;
+    const int Q = a.q_tiles;
+    const int F = a.past_items ? min(a.fetchers, Q) : 0;
+    const int ND = a.dev_q1 - a.dev_q0;
+    const int L = a.past_len[p / a.Hkv];
+    // query tiles go out last row first: under the causal mask later rows see more keys
+    if (r >= F && r < F + ND) {
+      const int qt = a.dev_q1 - 1 - (r - F);
+      // the storer role: this item's query tile's tokens' new K/V rows go to the host cache (each
+      // query tile has exactly one own-key item, so every new row is written once)
+      if (a.store_new) s0 = qt * TPT, s1 = min((qt + 1) * TPT, a.T);
+      it = AttnItem{p, qt, L, L + a.T, 1, a.dev_final, 0, a.nstate};
+      nt = a.past_items != 0;
+    } else {
+      const int qt = Q - 1 - (r < F ? r : r - ND);
+      const int kc1 = a.clip_past ? min(a.kc1, L) : a.kc1;
+      it = AttnItem{p, qt, a.kc0, kc1, a.first, a.last, a.merge_new, a.state};
+    }
   }
+  if (s1 > s0) attn_store<T, DH, PAGED>(a, it.p, s0, s1);
+  if (nt) attn_item<T, DH, G, PAGED, true>(a, it, lds);
+  else attn_item<T, DH, G, PAGED, false>(a, it, lds);
 }
 
 template <typename T, int DH, int G, bool PAGED>
