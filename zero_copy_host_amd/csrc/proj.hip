@@ -26,13 +26,16 @@
 namespace dkv {
 
 #ifndef DKV_PROJ_BK
-#define DKV_PROJ_BK 32   // reduction depth per LDS stage, 16-bit types (build-time tunable)
+#define DKV_PROJ_BK 64   // reduction depth per LDS stage, 16-bit types (build-time tunable)
 #endif
 #ifndef DKV_PROJ_NB
 #define DKV_PROJ_NB 4    // 32-column MFMA blocks per wave, 16-bit types (build-time tunable)
 #endif
 #ifndef DKV_PROJ_MB
 #define DKV_PROJ_MB 2    // 32-row MFMA blocks per wave, 16-bit types (build-time tunable)
+#endif
+#ifndef DKV_PROJ_SETS
+#define DKV_PROJ_SETS 1  // operand register sets, 16-bit types (2: loads two steps ahead instead of one)
 #endif
 #ifndef DKV_PROJ_WM
 #define DKV_PROJ_WM 4    // waves along M per workgroup, 16-bit types (build-time tunable; 2 columns of waves)
@@ -203,7 +206,7 @@ void proj_kernel(const ProjArgs a) {
   // Operand loads of reduction step kt into register set `set`. Every load is issued: rows
   // past M or past the segment read the last valid row instead (their products land in
   // outputs the epilogue never stores) and steps past the last read the last step, so each
-  // LDS store waits only for its own register set, two steps after the loads were issued.
+  // LDS store waits only for its own register set, SETS steps after the loads were issued.
   const int nk = D / BK;
   const int mlast = a.M - 1, nlast = nseg - 1;
   // (two named register sets chosen by a branch, never an array indexed by the set, which
@@ -251,8 +254,12 @@ void proj_kernel(const ProjArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // step kt computes from LDS buffer kt % 2; register set 0 carries steps 1, 3, 5, ... and set
-  // 1 steps 2, 4, 6, ... (loaded two steps ahead, stored to LDS one step ahead)
+  // step kt computes from LDS buffer kt % 2. 16-bit types: one register set (SETS = 1) carries
+  // step kt + 1's operands, loaded during step kt - 1 and stored to LDS during step kt: at 64-deep
+  // steps one step of products covers the load latency, and the second set would spill (70B-shaped
+  // projection 5.59 -> 5.11-5.24 ms against 32-deep steps with two sets; 8B-shaped the same).
+  // fp32 keeps two sets: set 0 carries steps 1, 3, 5, ... and set 1 steps 2, 4, 6, ... (loaded
+  // two steps ahead, stored to LDS one step ahead).
   auto step = [&](const int kt, const int buf, const int set) __attribute__((always_inline)) {
     const T* tX = sX + buf * C::TILE_X;
     const T* tW = sW + buf * C::TILE_W;
@@ -271,14 +278,15 @@ void proj_kernel(const ProjArgs a) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(fa[i], fb[j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1, set);
-    gload(set, kt + 3);
+    constexpr int SETS = sizeof(T) == 2 ? DKV_PROJ_SETS : 2;
+    if (kt + 1 < nk) sstore(buf ^ 1, SETS == 2 ? set : 0);
+    gload(SETS == 2 ? set : 0, kt + 1 + SETS);
     __syncthreads();
   };
   gload(0, 0);
   sstore(0, 0);
   gload(0, 1);
-  gload(1, 2);
+  if (sizeof(T) != 2 || DKV_PROJ_SETS == 2) gload(1, 2);
   __syncthreads();
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {   // whole pairs of steps, no exit mid-body
