@@ -54,8 +54,9 @@ extern "C" {
  *   DIRECTKV_PREFILL_CHUNKED=0     prefills with several super-chunks and query tiles take one
  *                                  launch per super-chunk instead of the two-launch form (a
  *                                  chunk launch of every super-chunk's items, then a finish
- *                                  launch); rounding order changes, not the result within
- *                                  tolerance;
+ *                                  launch), and attn_workspace_bytes leaves out the two-launch
+ *                                  form's running states (at most 2 GiB); rounding order
+ *                                  changes, not the result within tolerance;
  *   DIRECTKV_PREFILL_INSERT=<n>    two-launch form: items of a super-chunk dispatched before
  *                                  the next one's fetchers (dispatch order only: bitwise the
  *                                  same output);

@@ -200,6 +200,20 @@ def test_workspace_two_launch_prefill_region(dkv):
     assert ws(1, 8, 8192 + 3073, 8192, 32) == base(1, 8, 8192, 32) + 2 * state(1, 8, 8192, 4)
 
 
+def test_workspace_without_two_launch_prefill(dkv, monkeypatch):
+    """DIRECTKV_PREFILL_CHUNKED=0 keeps the launch-per-super-chunk path and the workspace query
+    then leaves the super-chunk states out (the 8B-shaped prefill: 1.49 GB -> 382 MB)."""
+    L = dkv.lib()
+    c = _fake_cache(dkv, B=1, Hkv=8, d=128, cap=32768)
+    lens, lp = _lens([24576])
+    with_states = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
+    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNKED", "0")
+    without = L.attn_workspace_bytes(0, ctypes.byref(c), 1, 8192, 32, lp)
+    state = 8 * (8192 * 4 // 32) * (4 * 16 + 2) * 64 * 4
+    assert with_states - without == 8 * state
+    assert without < 400 * 10 ** 6
+
+
 # ---- paged cache: the block table is checked on the host before anything is enqueued
 
 PAGED_MAGIC = 0x444B5650   # the mark kv_paged_alloc_host leaves in a descriptor

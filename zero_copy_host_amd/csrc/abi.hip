@@ -346,7 +346,9 @@ int prefill_fetchers() {
 // a second launch runs the heavier own-key items, which fold every state in as they finalise.
 // Two super-chunks then share an XCD's L2, three eighths of it each. It is used where every
 // super-chunk's state fits kChunkStateCap of workspace (not for a paged cache), else the
-// launch-per-super-chunk path runs (DIRECTKV_PREFILL_CHUNKED=0 forces that path).
+// launch-per-super-chunk path runs (DIRECTKV_PREFILL_CHUNKED=0 forces that path, and the workspace
+// query then leaves the states out: the mode trades up to kChunkStateCap of workspace, reused by
+// every call on a stream, for the overlap).
 constexpr size_t kChunkStateCap = (size_t)2 << 30;
 
 int chunk_group(int P) { return P % 8 == 0 ? 8 : P; }
@@ -370,7 +372,7 @@ bool chunked_enabled() {
 // super-chunk states the workspace holds for the two-launch prefill: enough for any past length
 // up to capacity - T, or 0 where the mode is not used
 int chunked_max(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads, bool paged) {
-  if (paged || c->n_kv_heads <= 0) return 0;
+  if (paged || c->n_kv_heads <= 0 || !chunked_enabled()) return 0;
   const int G = std::max(1, n_q_heads / c->n_kv_heads);
   if ((long long)T * G <= attn_rows_per_tile()) return 0;   // one query tile per pair: key splits
   const long long max_past = (long long)c->capacity - T;
