@@ -15,7 +15,8 @@
 // query tiles. Each workgroup keeps 256 query rows in registers (8 waves x 32), sweeps the
 // super-chunk through double-buffered LDS tiles (loads issued two tiles ahead), and carries
 // the per-row softmax state (o, m, l) in device memory from one super-chunk launch to the
-// next. Keys below past_len[b] come from the host cache; this step's new keys come from the
+// next (or, in the two-launch form, leaves one state per super-chunk for a finish launch to
+// merge). Keys below past_len[b] come from the host cache; this step's new keys come from the
 // device copy the projection left, so they never cross the link a second time. The launch
 // (or launches) whose keys hold no host rows also writes this step's new rows to the host
 // cache (the storer role), a share each.
@@ -34,9 +35,6 @@ namespace dkv {
 // Build-time tunables (defaults are the tuned values).
 #ifndef DKV_ATTN_KT
 #define DKV_ATTN_KT 64
-#endif
-#ifndef DKV_ATTN_SETPRIO
-#define DKV_ATTN_SETPRIO 0
 #endif
 #ifndef DKV_ATTN_WAVES
 #define DKV_ATTN_WAVES 8   // waves per workgroup, 32 query rows each
