@@ -114,7 +114,7 @@ def cpu_model():
 
 
 def _oracle_threads():
-    """Threads for the C oracle: the host cores this process may use, at most 16 (a one-GPU box's
+    """Threads for the C oracle: the host cores this process may use, at most 16 (a one-GPU machine's
     share of its host)."""
     try:
         n = len(os.sched_getaffinity(0))

@@ -9,7 +9,7 @@ key positions: the maximum of a query row is raised 8-11 times over a few thousa
 several launches, and the scores of this step's new keys are large as well.
 
 Every input and every query-key product is exact in the three dtypes, so the GPU's rounding of
-Q to bf16/f16 for the matrix cores loses nothing and the benchmark spec's tolerances apply unchanged:
+Q to bf16/f16 for the matrix cores loses nothing and the parity tolerances apply unchanged:
 max-abs 2e-2 and mean-abs 2e-3 for bf16/f16, 1e-5 for fp32, against the fp64 oracle. The new
 K/V rows are exact too, so the appended rows are compared bit for bit."""
 import numpy as np

@@ -330,7 +330,7 @@ int superchunk_keys(const dkv_cache* c, int32_t pairs, bool paged, int32_t q_til
 // Past-key items per pair dispatched ahead of a launch's own-key items: they bring the launch's
 // super-chunk over the host link into L2 while the own-key items compute, and compute at the
 // link's pace themselves (DIRECTKV_PREFILL_FETCHERS overrides it for tuning). 8B-shaped prefill,
-// one box: 0, 1, 2, 4, 8 fetchers per pair (per XCD) 5.19, 5.51, 5.50, 5.13, 5.10 ms; the
+// one machine: 0, 1, 2, 4, 8 fetchers per pair (per XCD) 5.19, 5.51, 5.50, 5.13, 5.10 ms; the
 // 70B-shaped prefill, link-hidden either way, 66.8-67.2 ms for all.
 int prefill_fetchers() {
   if (const char* env = getenv("DIRECTKV_PREFILL_FETCHERS")) {
