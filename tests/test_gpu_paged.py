@@ -155,13 +155,13 @@ def test_paged_decode_equals_contiguous_bitwise(dtype, d, G):
     compare(out_p, ref, dtype, f"paged decode {dtype} d{d} G{G}")
 
 
-@pytest.mark.parametrize("chunk", [None, "64"])
-def test_paged_prefill_equals_contiguous_bitwise(chunk, monkeypatch):
+@pytest.mark.parametrize("chunk,two_launch", [(None, "0"), ("64", "0"), ("64", "1")])
+def test_paged_prefill_equals_contiguous_bitwise(chunk, two_launch, monkeypatch):
     """Several super-chunks (chunk 64: many launches, the new rows stored by several of
-    them), ragged query tiles, two sequences of different lengths. A paged cache always takes the
-    launch-per-super-chunk path, so the contiguous run is held to that path too (the two-launch
-    prefill merges the super-chunks' states in another order)."""
-    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNKED", "0")
+    them), ragged query tiles, two sequences of different lengths; with the launch-per-super-chunk
+    path and with the two-launch form (three super-chunk states merged at the end), both caches
+    held to the same path and super-chunk size."""
+    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNKED", two_launch)
     if chunk:
         monkeypatch.setenv("DIRECTKV_PREFILL_CHUNK", chunk)
     case = _case(302, 2, 70, [33, 130], 256, 8, 2, 128, "bf16")

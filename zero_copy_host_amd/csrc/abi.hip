@@ -344,8 +344,8 @@ int prefill_fetchers() {
 // super-chunk, each leaving its own state, with the next super-chunk's fetchers dispatched while the
 // current one's items compute, so the link works beside the MFMA pipes instead of ahead of them;
 // a second launch runs the heavier own-key items, which fold every state in as they finalise.
-// Two super-chunks then share an XCD's L2, three eighths of it each. It is used where every
-// super-chunk's state fits kChunkStateCap of workspace (not for a paged cache), else the
+// Two super-chunks then share an XCD's L2, three eighths of it each (a quarter each for a paged
+// cache). It is used where every super-chunk's state fits kChunkStateCap of workspace, else the
 // launch-per-super-chunk path runs (DIRECTKV_PREFILL_CHUNKED=0 forces that path, and the workspace
 // query then leaves the states out: the mode trades up to kChunkStateCap of workspace, reused by
 // every call on a stream, for the overlap).
@@ -353,15 +353,18 @@ constexpr size_t kChunkStateCap = (size_t)2 << 30;
 
 int chunk_group(int P) { return P % 8 == 0 ? 8 : P; }
 
-int chunked_keys(const dkv_cache* c, int32_t group) {
+int chunked_keys(const dkv_cache* c, int32_t group, bool paged) {
+  // a paged super-chunk keeps the launch-per-super-chunk path's 1 MiB (its pages scatter over the
+  // pool, and an item stages at most kPagedSuperchunk keys' page ids)
+  const size_t limit = paged ? kPagedSuperchunk : 1 << 20;
   if (const char* env = getenv("DIRECTKV_PREFILL_CHUNK")) {
     const long v = strtol(env, nullptr, 10);
-    if (v >= 64) return (int)(v / 64 * 64);
+    if (v >= 64) return (int)std::min<size_t>(v / 64 * 64, limit);
   }
   const int per_xcd = std::max(1, (group + 7) / 8);
   const size_t row_bytes = 2 * (size_t)c->head_dim * elem_size(c->dtype);
-  const size_t keys = (size_t)(3u << 19) / ((size_t)per_xcd * row_bytes);
-  return (int)std::max<size_t>(64, keys / 64 * 64);
+  const size_t keys = (size_t)(paged ? (1u << 20) : (3u << 19)) / ((size_t)per_xcd * row_bytes);
+  return (int)std::min<size_t>(std::max<size_t>(64, keys / 64 * 64), limit);
 }
 
 bool chunked_enabled() {
@@ -370,13 +373,14 @@ bool chunked_enabled() {
 }
 
 // super-chunk states the workspace holds for the two-launch prefill: enough for any past length
-// up to capacity - T, or 0 where the mode is not used
+// up to capacity - T, or 0 where the mode is not used (a paged cache's view has capacity
+// max_pages x 16)
 int chunked_max(const dkv_cache* c, int32_t batch, int32_t T, int32_t n_q_heads, bool paged) {
-  if (paged || c->n_kv_heads <= 0 || !chunked_enabled()) return 0;
+  if (c->n_kv_heads <= 0 || !chunked_enabled()) return 0;
   const int G = std::max(1, n_q_heads / c->n_kv_heads);
   if ((long long)T * G <= attn_rows_per_tile()) return 0;   // one query tile per pair: key splits
   const long long max_past = (long long)c->capacity - T;
-  const int ck = chunked_keys(c, chunk_group(batch * c->n_kv_heads));
+  const int ck = chunked_keys(c, chunk_group(batch * c->n_kv_heads), paged);
   const long long S = (max_past + ck - 1) / ck;
   const size_t sb = round_up(attn_state_bytes(c->head_dim, batch, c->n_kv_heads, T, G), 256);
   if (S < 2 || (size_t)S * sb > kChunkStateCap) return 0;
@@ -707,11 +711,11 @@ int run_prefill(const dkv_cache* c, const Paging& pg, const void* x, const void*
     }
     {
       // the two-launch prefill, where its super-chunks' states fit the workspace
-      const int ck = chunked_keys(c, group);
+      const int ck = chunked_keys(c, group, paged);
       const int nc = max_past > 0 ? (max_past + ck - 1) / ck : 0;
       const int ckp = nc > 0 ? std::min<int>(ck, (int)round_up((max_past + nc - 1) / nc, 64)) : ck;
       const int SC = nc > 0 ? (max_past + ckp - 1) / ckp : 0;
-      if (!paged && SC >= 2 && SC <= lay.n_chunks && chunked_enabled()) {
+      if (SC >= 2 && SC <= lay.n_chunks && chunked_enabled()) {
         int qa = 0;
         const double goal = cum[Q] * chunked_own_percent() / 100.0;
         while (qa < Q && cum[qa + 1] <= goal + 1e-9) ++qa;
