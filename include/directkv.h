@@ -169,7 +169,10 @@ int attn_prefill(const dkv_cache* c, const void* x, const void* wq, const void* 
  *                        kv head) pairs ([N] Key Idea (3), warp-level pipelining: a producer
  *                        streams the next key super-chunk over the link while the current one
  *                        is computed). Currently DISABLED: every call returns UNSUPPORTED, since
- *                        its launch did not complete on the GPU and the cause is not found.
+ *                        its launch did not complete on the GPU and the cause is not found. The
+ *                        fused path's two-launch form (see DIRECTKV_PREFILL_CHUNKED) overlaps
+ *                        the next super-chunk's transfer with the current one's compute instead,
+ *                        with no workgroup waiting for another.
  * Errors: as attn_prefill, plus INVALID_ARG for an unknown variant.
  */
 enum {
