@@ -235,6 +235,29 @@ def test_decode_at_the_batch_limit(monkeypatch):
 
 # ------------------------------------------------------------------ prefill
 
+
+@pytest.mark.parametrize("two_launch", ["1", "0"], ids=["two-launch", "per-chunk"])
+def test_prefill_at_the_batch_limit(two_launch, monkeypatch):
+    """256 sequences (the most one call takes), ragged pasts from 0 to 300, 2 query tiles per
+    (sequence, kv head) pair (512 pairs), 64-key super-chunks: up to 5 of them per sequence,
+    empty ones for the short pasts. Sampled rows against the oracle; the appended rows of the first,
+    middle and last sequences within the accumulation bound."""
+    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNKED", two_launch)
+    monkeypatch.setenv("DIRECTKV_PREFILL_CHUNK", "64")
+    B, T, D, Hq, Hkv, d, dtype = 256, 40, 128, 16, 2, 64, "bf16"
+    past = [int(v) for v in synth.Draw(24).lengths(B, 0, 300)]
+    past[0], past[1], past[-1] = 0, 64, 300
+    case = _case(24, B, T, past, D, Hq, Hkv, d, dtype)
+    ts = np.array([0, 1, 19, 38, 39])
+    out, ref, kg, vg, kc, vc = _run_prefill(case, t_index=ts)
+    compare(out, ref, dtype, f"prefill B=256 two_launch={two_launch}")
+    ak = absdot_rows(case["x"], case["wk"], Hkv, d)
+    av = absdot_rows(case["x"], case["wv"], Hkv, d)
+    for b in (0, 1, 128, 255):
+        L = int(case["past_len"][b])
+        compare_rows(kg[b, :, L:L + T], kc[b, :, L:L + T], dtype, ak[b], D, f"new K rows of sequence {b}")
+        compare_rows(vg[b, :, L:L + T], vc[b, :, L:L + T], dtype, av[b], D, f"new V rows of sequence {b}")
+
 PREFILL_CASES = [
     # B, T, past, D, Hq, Hkv, d, dtype
     (1, 128, [0], 256, 4, 4, 64, "f32"),             # the tiny fp32 layer
