@@ -42,6 +42,8 @@ CASES = [
     (1, 97, [2100], 256, 8, 2, 128, "f32", 512),             # G = 4, fp32, d = 128
     (3, 130, [2600, 1200, 0], 256, 16, 4, 64, "bf16", 256),  # 12 pairs, 2 per XCD's L2, 11 super-chunks
     (2, 520, [900, 1800], 256, 8, 1, 128, "bf16", 128),      # G = 8, 17 query tiles, 15 super-chunks
+    (1, 64, [2000], 256, 8, 2, 128, "bf16", 256),            # T*G = 256: one query tile, key splits instead
+    (1, 65, [2000], 256, 8, 2, 128, "bf16", 256),            # T*G = 260: two query tiles, the last of 4 rows
 ]
 
 
