@@ -400,9 +400,9 @@ int chunked_own_percent() {
 // chunk j's items per pair dispatched ahead of chunk j+1's fetchers: five sixths of them, so the
 // next super-chunk crosses the link during the last sixth of this one's items and the fetchers'
 // own compute. Earlier, the two super-chunks and the running-state streams overflow L2: 8B-shaped
-// prefill (120 such items per pair) with 40, 100 and 120 read 1.153x, 1.014x and about 1.01x the
-// algorithmic host bytes, in 4.62-4.72 ms for all from 60 on (DIRECTKV_PREFILL_INSERT=<items>
-// overrides it for tuning).
+// prefill (120 such items per pair) with 40, 100 and 120 read 1.10-1.15x, 1.014-1.020x and
+// 1.01-1.04x the algorithmic host bytes over two runs, in 4.62-4.76 ms for all from 60 on
+// (DIRECTKV_PREFILL_INSERT=<items> overrides it for tuning).
 int chunked_insert(int items) {
   if (const char* env = getenv("DIRECTKV_PREFILL_INSERT")) {
     const long v = strtol(env, nullptr, 10);
